@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+One step = one serving step of the decode workload: append the newest token's
+K and V for every sequence (pkv_append), then paged decode attention over the
+whole cache (pkv_decode_attn). Workload: batch 64, 32 query / 8 KV heads,
+head dim 128, fp16 KV, 16-token blocks, context lengths uniform in
+[512, 4096], physical blocks shuffled (Llama-3-8B-shaped single layer).
+
+Printed as one JSON line:
+  value      decode KV-read GB/s = K+V bytes the step must read / step time
+  roofline   the decode kernel's own duration (HIP events on its stream)
+             against the HBM peak; traffic from rocprofv3 counters when they
+             match the current kernel sources (else null)
+  suffix_prefill  the same for the suffix-prefill workload (16 requests x
+             1,900 cached + 100 new tokens, bf16): TFLOP/s against bf16 MFMA peak
+  cpu_baseline    the CPU oracle timed on this host on the same decode workload
+
+Inputs are synthetic (seeded N(0,1)), resident in HBM before timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak
+KERNEL_SOURCES = ["prefix_reuse_amd/csrc/pkv_decode.hip", "prefix_reuse_amd/csrc/pkv_prefill.hip",
+                  "prefix_reuse_amd/csrc/pkv_device.hpp", "prefix_reuse_amd/csrc/pkv_append.hip"]
+
+
+def sources_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        h.update((ROOT / f).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name: str, files) -> dict | None:
+    """Counter-based HBM traffic per launch, if it was taken on these sources."""
+    p = ROOT / "profiles" / f"{name}_traffic.json"
+    if not p.exists():
+        return None
+    rec = json.loads(p.read_text())
+    if rec.get("sources_hash") != sources_hash(files):
+        return None
+    return rec
+
+
+class EventTimer:
+    """Average duration of repeated launches, measured with HIP events recorded
+    on the stream the kernels are launched on."""
+
+    def __init__(self, torch, stream, n):
+        self.torch = torch
+        self.stream = stream
+        self.pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(n)]
+        self.i = 0
+
+    def __enter__(self):
+        self.pairs[self.i][0].record(self.stream)
+        return self
+
+    def __exit__(self, *exc):
+        self.pairs[self.i][1].record(self.stream)
+        self.i += 1
+
+    def mean_ms(self) -> float:
+        self.torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in self.pairs[: self.i]) / max(self.i, 1)
+
+
+def decode_setup(torch, pkv, workloads, dev):
+    case = workloads.config2_llama_decode()
+    kc, vc = pkv.caches_from_logical(case.k_pool, case.v_pool, dev)
+    t = {
+        "case": case, "kc": kc, "vc": vc,
+        "q": case.q.to(dev), "bt": case.block_tables.to(dev), "cl": case.context_lens.to(dev),
+        "k_new": case.k_new.to(dev), "v_new": case.v_new.to(dev), "slots": case.slot_mapping.to(dev),
+    }
+    t["out"] = torch.empty_like(t["q"])
+    need = pkv.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                                      case.block_tables.shape[1], case.block_size)
+    t["ws"] = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+    return t
+
+
+def prefill_setup(torch, pkv, workloads, dev):
+    case = workloads.config4_suffix_prefill()
+    kc, vc = pkv.caches_from_logical(case.k_pool, case.v_pool, dev)
+    t = {
+        "case": case, "kc": kc, "vc": vc, "q": case.q_suffix.to(dev), "bt": case.block_tables.to(dev),
+        "pl": case.prefix_lens.to(dev), "sl": case.suffix_lens.to(dev),
+        "k_new": case.k_new.to(dev), "v_new": case.v_new.to(dev), "slots": case.slot_mapping.to(dev),
+    }
+    t["out"] = torch.empty_like(t["q"])
+    return t
+
+
+def run_decode_call(pkv, t):
+    c = t["case"]
+    pkv.decode_attn(t["q"], t["kc"], t["vc"], t["bt"], t["cl"], c.scale, out=t["out"], workspace=t["ws"])
+
+
+def run_prefill_call(pkv, t):
+    c = t["case"]
+    pkv.suffix_prefill_attn(t["q"], t["kc"], t["vc"], t["bt"], t["pl"], t["sl"], c.scale, out=t["out"])
+
+
+def cpu_baseline(case, min_seconds=10.0, max_seconds=30.0) -> dict:
+    """The oracle (as written) on the same decode step, repeated over the whole
+    batch until at least ``min_seconds`` of CPU work."""
+    import numpy as np
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
+    except Exception:  # pragma: no cover
+        threads = 1
+    kp = case.k_pool.double().numpy()
+    vp = case.v_pool.double().numpy()
+    kn = case.k_new.double().numpy()
+    vn = case.v_new.double().numpy()
+    q = case.q.double().numpy()
+    bt = case.block_tables.numpy()
+    cl = case.context_lens.numpy()
+    reps, t0 = 0, time.perf_counter()
+    seqs_done = 0
+    while True:
+        kc, vc = oracle.append(kp, vp, kn, vn, case.slot_mapping.numpy())
+        for s in range(case.num_seqs):
+            oracle.decode_attention(q, kc, vc, bt, cl, case.scale, seqs=[s])
+            seqs_done += 1
+            if time.perf_counter() - t0 > max_seconds:
+                break
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or el > max_seconds:
+            break
+    el = time.perf_counter() - t0
+    per_seq_bytes = cl.astype(np.int64) * 2 * case.num_kv_heads * case.head_dim * case.k_pool.element_size()
+    done_bytes = int(per_seq_bytes.sum()) * (seqs_done // case.num_seqs) + int(per_seq_bytes[: seqs_done % case.num_seqs].sum())
+    return {
+        "value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": f"float64 NumPy oracle (append + decode) over {seqs_done} sequence-steps of the same "
+                  f"64-sequence batch ({reps} pass(es), {el:.1f} s wall), bytes counted as in the GPU metric",
+        "seconds": round(el, 2), "cpu_count": os.cpu_count(),
+        "affinity": len(os.sched_getaffinity(0)),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+                    help="run only this kernel's launches (for profiler runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import prefix_reuse_amd as pkv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    if args.only is not None:
+        t = (decode_setup if args.only == "decode" else prefill_setup)(torch, pkv, workloads, dev)
+        call = run_decode_call if args.only == "decode" else run_prefill_call
+        for _ in range(args.warmup + args.steps):
+            call(pkv, t)
+        torch.cuda.synchronize()
+        # a plain copy of known size, to calibrate the memory counters
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "launches": args.warmup + args.steps, "copy_bytes": 1 << 30}))
+        return 0
+
+    # ---------------- decode step: append + decode ----------------
+    t = decode_setup(torch, pkv, workloads, dev)
+    case = t["case"]
+
+    def step():
+        pkv.append(t["k_new"], t["v_new"], t["slots"], t["kc"], t["vc"])
+        run_decode_call(pkv, t)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    kv_bytes = case.kv_read_bytes()
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # the decode kernel alone: events around each launch on its stream
+    timer = EventTimer(torch, stream, args.steps)
+    for _ in range(args.steps):
+        with timer:
+            run_decode_call(pkv, t)
+    dec_ms = timer.mean_ms()
+    dec_gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
+    traffic = load_traffic("decode_llama3_8b_b64_fp16", KERNEL_SOURCES)
+    roofline = {
+        "kernel": "pkv_decode_attn (decode_kernel + decode_combine_kernel)",
+        "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+        "traffic": None if traffic is None else traffic["bytes_per_launch"],
+        "avg_launch_us": round(dec_ms * 1e3, 2), "algorithmic_bytes_per_launch": kv_bytes,
+    }
+
+    result = {
+        "metric": "decode KV-read GB/s (% HBM peak) + suffix-prefill TFLOP/s (% MFMA), 1 GPU",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "llama3-8b-shaped decode step: append 1 token/seq + paged decode attention",
+                   "batch": case.num_seqs, "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads,
+                   "head_dim": case.head_dim, "block_size": case.block_size, "kv_dtype": "fp16",
+                   "context_lens": "uniform [512, 4096], seed 1002", "kv_bytes_per_step": kv_bytes,
+                   "tokens_per_step": case.num_seqs},
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(case.num_seqs / (ms_per_step * 1e-3), 1),
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+        "roofline": roofline,
+    }
+
+    # ---------------- suffix prefill: append suffix + prefill ----------------
+    if not args.no_prefill:
+        del t
+        torch.cuda.empty_cache()
+        p = prefill_setup(torch, pkv, workloads, dev)
+        pc = p["case"]
+        pkv.append(p["k_new"], p["v_new"], p["slots"], p["kc"], p["vc"])
+        for _ in range(args.warmup):
+            run_prefill_call(pkv, p)
+        timer = EventTimer(torch, stream, args.steps)
+        for _ in range(args.steps):
+            with timer:
+                run_prefill_call(pkv, p)
+        pre_ms = timer.mean_ms()
+        flops = pc.flops()
+        tflops = flops / (pre_ms * 1e-3) / 1e12
+        ptraffic = load_traffic("prefill_16x1900p100_bf16", KERNEL_SOURCES)
+        result["suffix_prefill"] = {
+            "metric": "suffix-prefill TFLOP/s", "value": round(tflops, 2), "unit": "TFLOP/s",
+            "config": {"workload": "16 requests x (1,900 cached + 100 new tokens), 32/8 heads, d=128, bf16, B=16",
+                       "flop_per_launch": flops, "suffix_tokens": int(pc.suffix_lens.sum())},
+            "roofline": {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tflops, 2),
+                         "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                         "traffic": None if ptraffic is None else ptraffic["bytes_per_launch"],
+                         "avg_launch_us": round(pre_ms * 1e3, 2)},
+            "suffix_tokens_per_s": round(int(pc.suffix_lens.sum()) / (pre_ms * 1e-3), 1),
+        }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case)
+
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,197 @@
+/*
+ * pkv.h — C ABI of libpkv: attention over a paged KV cache with prefix reuse,
+ * hand-written HIP kernels for MI355X (gfx950).
+ *
+ * Source of the operations (pages, cited by title and section):
+ *  [A] "PagedAttention과 RadixAttention으로 LLM KV 캐시 최적화" (aitrends.kr):
+ *      §02 fixed 16/32-token blocks, a per-request block table mapping logical
+ *      blocks to scattered physical blocks that the attention kernel reads as
+ *      one contiguous sequence; §03 reuse of the longest cached prefix so only
+ *      the suffix is computed; §05 reuse leaves the model output unchanged.
+ *  [B] "KV Cache 완전 정리 — PagedAttention vs RadixAttention" (cell-devlog):
+ *      "FP8 KV 캐시" — the cache may be stored as fp8 e4m3.
+ *  [C] "KV Cache에 대해 알아보자 (Feat. Attention)" (chooblog): §1 the
+ *      attention equation softmax(QK^T / sqrt(d_k)) V; §3 prefill processes
+ *      all new tokens at once, decode appends the new token's K, V and attends
+ *      over the whole cache; §4 grouped-query attention (fewer KV heads).
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ *  - Every tensor is described by a pkv_tensor: a DEVICE pointer owned by the
+ *    caller, a dtype, and shape/strides in ELEMENTS. The library never
+ *    allocates, frees or retains device memory; pointers are used only by work
+ *    enqueued during the call.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns without synchronising. Buffers must outlive that work.
+ *  - Validation is host-side only: the library never reads device memory to
+ *    validate and never synchronises. On error nothing is launched, a status
+ *    other than PKV_OK is returned and pkv_last_error() describes it.
+ *  - Device-side values are clamped, not trusted: a block id outside
+ *    [0, num_blocks) is clamped into range, a length past a table's capacity is
+ *    cut to the capacity, a negative length counts as 0, and a slot outside
+ *    [0, num_blocks*B) is skipped. Results for such inputs are unspecified but
+ *    every memory access stays inside the caller's buffers.
+ *  - Thread safety: no global mutable state other than the thread-local error
+ *    string; concurrent calls on different streams are safe.
+ *
+ * Physical cache layout (the pages leave it open; this library's choice)
+ * ----------------------------------------------------------------------
+ *  A token's SLOT is physical_block * B + offset_in_block ([A] §02). The K and
+ *  V caches of one layer are two contiguous tensors:
+ *     k_cache: [num_blocks, H_kv, B, d]   one (block, head) = B rows of d
+ *     v_cache: [num_blocks, H_kv, d, B]   one (block, head) = d rows of B tokens
+ *  i.e. each (block, KV head) is one contiguous tile, and V tiles are stored
+ *  transposed so that both attention products read their matrix-core operands
+ *  with 16-byte loads. Element of token `slot`, head h, dim i:
+ *     K: k_cache[slot / B][h][slot % B][i]     V: v_cache[slot / B][h][i][slot % B]
+ *  Supported: d in {64, 128}, B in {16, 32}; cache dtype f32, f16, bf16 (same
+ *  as q) or fp8 e4m3fn (q in f16 or bf16; values are code * scale).
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+typedef enum {
+  PKV_F32 = 0,
+  PKV_F16 = 1,
+  PKV_BF16 = 2,
+  PKV_FP8_E4M3FN = 3, /* OCP e4m3fn: bias 7, no infinities, 0x7F/0xFF NaN, max 448 */
+  PKV_I32 = 4,
+  PKV_I64 = 5
+} pkv_dtype;
+
+typedef struct {
+  void* data;        /* device pointer */
+  int32_t dtype;     /* a pkv_dtype */
+  int32_t ndim;      /* 1..4 */
+  int64_t shape[4];
+  int64_t stride[4]; /* in elements */
+} pkv_tensor;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,        /* a required pointer is NULL */
+  PKV_ERR_DTYPE = 2,       /* unsupported dtype or dtype combination */
+  PKV_ERR_SHAPE = 3,       /* shapes disagree with each other */
+  PKV_ERR_LAYOUT = 4,      /* strides / alignment not supported */
+  PKV_ERR_UNSUPPORTED = 5, /* head_dim, block size or head grouping not supported */
+  PKV_ERR_WORKSPACE = 6,   /* decode workspace missing or too small */
+  PKV_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
+} pkv_status;
+
+/*
+ * pkv_append — write new tokens' K and V rows into their cache slots.
+ * [C] §3 (decode adds the new token's K, V to the cache; prefill writes the
+ * K, V of every new token); [A] §02 (the slot comes from the block table).
+ *
+ *  k, v          [T, H_kv, d], dtype f32/f16/bf16; last dim contiguous,
+ *                row starts 16-byte aligned.
+ *  slot_mapping  [T] int32 or int64; row i goes to slot slot_mapping[i].
+ *                Negative (or out-of-range) slots are skipped. Two rows naming
+ *                the same slot in one call: which one lands is unspecified.
+ *  k_cache       [num_blocks, H_kv, B, d] contiguous (layout above).
+ *  v_cache       [num_blocks, H_kv, d, B] contiguous.
+ *  k_scale,      used only for fp8 caches: the stored code is
+ *  v_scale       e4m3fn(x / scale), the float32 quotient rounded to nearest
+ *                with ties to even and saturated to +-448. Must be > 0.
+ *                For other caches the row dtype must equal the cache dtype and
+ *                the copy is bit-exact.
+ * Bytes not named by a slot are never written.
+ */
+int pkv_append(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* slot_mapping,
+               const pkv_tensor* k_cache, const pkv_tensor* v_cache, float k_scale,
+               float v_scale, void* stream);
+
+/*
+ * pkv_decode_workspace_bytes — bytes of device workspace pkv_decode_attn needs
+ * for this problem size on the CURRENT device (the split count it picks
+ * depends on the device's compute-unit count; the environment variable
+ * PKV_DECODE_SPLIT_LEN, a positive multiple of 128, forces the context split
+ * length in tokens for both calls). Returns 0 on invalid sizes and when no
+ * split is needed.
+ */
+size_t pkv_decode_workspace_bytes(int64_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int64_t max_blocks_per_seq,
+                                  int32_t block_size);
+
+/*
+ * pkv_decode_attn — one decode step of paged attention.
+ * [C] §3: the new token's query attends to every cached K, V of its sequence;
+ * [C] §1: out = softmax(scale * q K^T) V; [C] §4: query head h reads KV head
+ * h / G with G = H_q / H_kv; [A] §02: token t of sequence s lives in physical
+ * block block_tables[s][t / B] at offset t % B.
+ *
+ *  q             [num_seqs, H_q, d], f32/f16/bf16; last dim contiguous, rows
+ *                16-byte aligned.
+ *  k_cache,      caches in the layout above.
+ *  v_cache
+ *  block_tables  [num_seqs, max_blocks] int32, row stride >= max_blocks; only
+ *                the first ceil(context_lens[s] / B) entries are read.
+ *  context_lens  [num_seqs] int32: cached tokens of each sequence, including
+ *                the newest one. 0 gives a zero output row.
+ *  scale         softmax scale (1/sqrt(d) in the usual model).
+ *  k_scale,      dequantization scales of an fp8 cache (ignored otherwise).
+ *  v_scale
+ *  workspace     device buffer of at least pkv_decode_workspace_bytes(...)
+ *                bytes (the caller allocates it; it holds per-split partial
+ *                results). May be NULL only if that function returns 0.
+ *  out           [num_seqs, H_q, d], same dtype as q; last dim contiguous.
+ * Results are bitwise deterministic and depend only on logical positions, so
+ * permuting physical blocks or aliasing identical blocks between sequences
+ * does not change a single bit.
+ */
+int pkv_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_tensor* v_cache,
+                    const pkv_tensor* block_tables, const pkv_tensor* context_lens, float scale,
+                    float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                    const pkv_tensor* out, void* stream);
+
+/*
+ * pkv_suffix_prefill_attn — attention for the new suffix tokens of requests
+ * whose prefix is already cached.
+ * [A] §03: with the longest matching prefix reused from the cache, only the
+ * unmatched suffix is computed; [C] §3: prefill handles all new tokens at
+ * once; [C] §1: the attention equation. Suffix row i of request r (absolute
+ * position P_r + i) attends to key positions 0 .. P_r + i inclusive: the whole
+ * prefix and the suffix causally. The suffix K, V must already be in the cache
+ * (pkv_append them first).
+ *
+ *  q_suffix      [sum_r S_r, H_q, d] packed request by request; f16/bf16
+ *                (or f32 with an f32 cache); rows 16-byte aligned.
+ *  k_cache,      caches in the layout above.
+ *  v_cache
+ *  block_tables  [R, max_blocks] int32; request r reads entries
+ *                0 .. ceil((P_r + S_r) / B) - 1.
+ *  prefix_lens   [R] int32, P_r >= 0.
+ *  suffix_lens   [R] int32, S_r >= 0; sum_r S_r must equal q_suffix.shape[0]
+ *                (the device values are trusted only up to that total).
+ *  scale,        as for pkv_decode_attn.
+ *  k_scale,
+ *  v_scale
+ *  out           [sum_r S_r, H_q, d], same dtype as q_suffix.
+ */
+int pkv_suffix_prefill_attn(const pkv_tensor* q_suffix, const pkv_tensor* k_cache,
+                            const pkv_tensor* v_cache, const pkv_tensor* block_tables,
+                            const pkv_tensor* prefix_lens, const pkv_tensor* suffix_lens,
+                            float scale, float k_scale, float v_scale, const pkv_tensor* out,
+                            void* stream);
+
+/* Description of the last error on the calling thread ("" if none). The
+ * pointer stays valid until the next pkv_* call on this thread. */
+const char* pkv_last_error(void);
+
+/* PKV_ABI_VERSION of the loaded library. */
+int pkv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

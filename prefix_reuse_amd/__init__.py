@@ -1,0 +1,195 @@
+"""Paged-KV attention with prefix reuse on MI355X: Python binding of libpkv.
+
+Argument marshalling only: every computation runs in the HIP kernels of
+``libpkv.so`` (built in-tree by ``prefix_reuse_amd.build``). PyTorch provides
+device memory and the current stream. If the library is missing this module
+raises at import; there is no fallback.
+
+Physical cache layout (see include/pkv.h): ``k_cache[num_blocks, H_kv, B, d]``
+and ``v_cache[num_blocks, H_kv, d, B]``; a token's slot is
+``physical_block * B + offset``. ``k_logical``/``v_logical`` give views in the
+order ``[num_blocks, B, H_kv, d]``.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "lib", "PkvError",
+    "append", "decode_attn", "suffix_prefill_attn", "decode_workspace_bytes",
+    "empty_caches", "caches_from_logical", "k_logical", "v_logical", "abi_version",
+]
+
+LIB_PATH = Path(__file__).resolve().parent / "libpkv.so"
+
+_DT = {
+    torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float8_e4m3fn: 3,
+    torch.int32: 4, torch.int64: 5,
+}
+
+
+class PkvTensor(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("ndim", ctypes.c_int32),
+        ("shape", ctypes.c_int64 * 4),
+        ("stride", ctypes.c_int64 * 4),
+    ]
+
+
+class PkvError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed with status {code}: {msg}")
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not LIB_PATH.exists():
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m prefix_reuse_amd.build` "
+            "(hipcc, gfx950). There is no CPU fallback.")
+    L = ctypes.CDLL(str(LIB_PATH))
+    P = ctypes.POINTER(PkvTensor)
+    L.pkv_append.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
+    L.pkv_append.restype = ctypes.c_int
+    L.pkv_decode_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]
+    L.pkv_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.pkv_decode_attn.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                  ctypes.c_void_p, ctypes.c_size_t, P, ctypes.c_void_p]
+    L.pkv_decode_attn.restype = ctypes.c_int
+    L.pkv_suffix_prefill_attn.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_float,
+                                          ctypes.c_float, P, ctypes.c_void_p]
+    L.pkv_suffix_prefill_attn.restype = ctypes.c_int
+    L.pkv_last_error.argtypes = []
+    L.pkv_last_error.restype = ctypes.c_char_p
+    L.pkv_abi_version.argtypes = []
+    L.pkv_abi_version.restype = ctypes.c_int
+    return L
+
+
+lib = _load()
+
+
+def abi_version() -> int:
+    return lib.pkv_abi_version()
+
+
+def _desc(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    if t.dim() > 4:
+        raise ValueError("at most 4 dims")
+    d = PkvTensor()
+    d.data = t.data_ptr() if t.numel() > 0 else 0
+    d.dtype = _DT[t.dtype]
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _ref(d):
+    return ctypes.byref(d) if d is not None else None
+
+
+def _stream(device: torch.device) -> int:
+    if device.type != "cuda":
+        raise ValueError("tensors must live on a GPU")
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise PkvError(fn, rc, lib.pkv_last_error().decode())
+
+
+# ---------------------------------------------------------------------------
+# cache allocation and layout views (plumbing)
+# ---------------------------------------------------------------------------
+def empty_caches(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
+                 dtype: torch.dtype, device="cuda") -> Tuple[torch.Tensor, torch.Tensor]:
+    k = torch.empty(num_blocks, num_kv_heads, block_size, head_dim, dtype=dtype, device=device)
+    v = torch.empty(num_blocks, num_kv_heads, head_dim, block_size, dtype=dtype, device=device)
+    return k, v
+
+
+def k_logical(k_cache: torch.Tensor) -> torch.Tensor:
+    """View [num_blocks, B, H_kv, d] of a physical K cache."""
+    return k_cache.permute(0, 2, 1, 3)
+
+
+def v_logical(v_cache: torch.Tensor) -> torch.Tensor:
+    """View [num_blocks, B, H_kv, d] of a physical V cache."""
+    return v_cache.permute(0, 3, 1, 2)
+
+
+def caches_from_logical(k_pool: torch.Tensor, v_pool: torch.Tensor, device="cuda"):
+    """Physical caches holding the contents of logical [NB, B, H_kv, d] pools."""
+    k = k_pool.permute(0, 2, 1, 3).contiguous().to(device)
+    v = v_pool.permute(0, 2, 3, 1).contiguous().to(device)
+    return k, v
+
+
+# ---------------------------------------------------------------------------
+# the three operations
+# ---------------------------------------------------------------------------
+def append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+           v_cache: torch.Tensor, k_scale: float = 1.0, v_scale: float = 1.0) -> None:
+    """Write rows k[i], v[i] ([T, H_kv, d]) into slot slot_mapping[i] of the caches."""
+    dk, dv, ds, dkc, dvc = map(_desc, (k, v, slot_mapping, k_cache, v_cache))
+    rc = lib.pkv_append(_ref(dk), _ref(dv), _ref(ds), _ref(dkc), _ref(dvc), float(k_scale),
+                        float(v_scale), _stream(k_cache.device))
+    _check("pkv_append", rc)
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                           max_blocks_per_seq: int, block_size: int) -> int:
+    return int(lib.pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                              max_blocks_per_seq, block_size))
+
+
+def decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                out: Optional[torch.Tensor] = None, k_scale: float = 1.0, v_scale: float = 1.0,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One paged decode step; returns ``out`` [num_seqs, H_q, d]."""
+    if out is None:
+        out = torch.empty_like(q)
+    block_size = k_cache.shape[2]
+    need = decode_workspace_bytes(q.shape[0], q.shape[1], k_cache.shape[1], q.shape[2],
+                                  block_tables.shape[1], block_size)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if (need and workspace is not None) else None
+    ws_bytes = workspace.numel() * workspace.element_size() if (need and workspace is not None) else 0
+    dq, dkc, dvc, dbt, dcl, do = map(_desc, (q, k_cache, v_cache, block_tables, context_lens, out))
+    rc = lib.pkv_decode_attn(_ref(dq), _ref(dkc), _ref(dvc), _ref(dbt), _ref(dcl), float(scale),
+                             float(k_scale), float(v_scale), ws_ptr, ws_bytes, _ref(do),
+                             _stream(q.device))
+    _check("pkv_decode_attn", rc)
+    return out
+
+
+def suffix_prefill_attn(q_suffix: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        block_tables: torch.Tensor, prefix_lens: torch.Tensor,
+                        suffix_lens: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
+                        k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
+    """Attention of the packed suffix rows over their cached prefix + causal suffix."""
+    if out is None:
+        out = torch.empty_like(q_suffix)
+    dq, dkc, dvc, dbt, dp, dsl, do = map(_desc, (q_suffix, k_cache, v_cache, block_tables,
+                                                  prefix_lens, suffix_lens, out))
+    rc = lib.pkv_suffix_prefill_attn(_ref(dq), _ref(dkc), _ref(dvc), _ref(dbt), _ref(dp), _ref(dsl),
+                                     float(scale), float(k_scale), float(v_scale), _ref(do),
+                                     _stream(q_suffix.device))
+    _check("pkv_suffix_prefill_attn", rc)
+    return out

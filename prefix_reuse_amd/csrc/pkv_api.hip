@@ -1,0 +1,339 @@
+// extern "C" entry points of libpkv: host-side validation of the tensor
+// descriptors, launch planning and kernel launches on the caller's stream.
+// Nothing here reads device memory or synchronises.
+#include "../../include/pkv.h"
+#include "pkv_internal.hpp"
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int ok() {
+  g_error.clear();
+  return PKV_OK;
+}
+
+size_t dtype_size(int dt) {
+  switch (dt) {
+    case PKV_F32: return 4;
+    case PKV_F16: return 2;
+    case PKV_BF16: return 2;
+    case PKV_FP8_E4M3FN: return 1;
+    case PKV_I32: return 4;
+    case PKV_I64: return 8;
+    default: return 0;
+  }
+}
+
+const char* dtype_name(int dt) {
+  switch (dt) {
+    case PKV_F32: return "f32";
+    case PKV_F16: return "f16";
+    case PKV_BF16: return "bf16";
+    case PKV_FP8_E4M3FN: return "fp8_e4m3fn";
+    case PKV_I32: return "i32";
+    case PKV_I64: return "i64";
+    default: return "?";
+  }
+}
+
+// Basic sanity of a descriptor: non-null, known dtype, expected rank.
+int check_tensor(const pkv_tensor* t, const char* name, int ndim) {
+  if (!t) return fail(PKV_ERR_NULL, "%s: descriptor is NULL", name);
+  if (dtype_size(t->dtype) == 0) return fail(PKV_ERR_DTYPE, "%s: unknown dtype %d", name, t->dtype);
+  if (t->ndim != ndim) return fail(PKV_ERR_SHAPE, "%s: expected %d dims, got %d", name, ndim, t->ndim);
+  for (int i = 0; i < ndim; ++i)
+    if (t->shape[i] < 0) return fail(PKV_ERR_SHAPE, "%s: negative extent in dim %d", name, i);
+  int64_t numel = 1;
+  for (int i = 0; i < ndim; ++i) numel *= t->shape[i];
+  if (numel > 0 && !t->data) return fail(PKV_ERR_NULL, "%s: data pointer is NULL", name);
+  return PKV_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Rows of a [n, heads, d] tensor: last dim contiguous, row starts 16-byte aligned.
+int check_rows(const pkv_tensor* t, const char* name) {
+  if (t->shape[2] > 1 && t->stride[2] != 1) return fail(PKV_ERR_LAYOUT, "%s: last dim must be contiguous", name);
+  const size_t es = dtype_size(t->dtype);
+  const bool s0 = t->shape[0] <= 1 || (t->stride[0] * (int64_t)es) % 16 == 0;
+  const bool s1 = t->shape[1] <= 1 || (t->stride[1] * (int64_t)es) % 16 == 0;
+  if (!aligned16(t->data) || !s0 || !s1)
+    return fail(PKV_ERR_LAYOUT, "%s: rows must start on 16-byte boundaries", name);
+  return PKV_OK;
+}
+
+struct CacheGeom {
+  int64_t num_blocks;
+  int32_t hkv, block, dim;
+  int dtype;
+};
+
+// k_cache [NB, Hkv, B, D] and v_cache [NB, Hkv, D, B], both contiguous.
+int check_caches(const pkv_tensor* kc, const pkv_tensor* vc, CacheGeom* g) {
+  int rc;
+  if ((rc = check_tensor(kc, "k_cache", 4))) return rc;
+  if ((rc = check_tensor(vc, "v_cache", 4))) return rc;
+  if (kc->dtype != vc->dtype) return fail(PKV_ERR_DTYPE, "k_cache and v_cache dtypes differ");
+  if (kc->dtype == PKV_I32 || kc->dtype == PKV_I64) return fail(PKV_ERR_DTYPE, "cache dtype must be floating point");
+  const int64_t nb = kc->shape[0], h = kc->shape[1], b = kc->shape[2], d = kc->shape[3];
+  if (vc->shape[0] != nb || vc->shape[1] != h || vc->shape[2] != d || vc->shape[3] != b)
+    return fail(PKV_ERR_SHAPE, "v_cache must be [num_blocks, H_kv, d, B] matching k_cache [num_blocks, H_kv, B, d]");
+  if (!(d == 64 || d == 128)) return fail(PKV_ERR_UNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)d);
+  if (!(b == 16 || b == 32)) return fail(PKV_ERR_UNSUPPORTED, "block size %lld not supported (16 or 32)", (long long)b);
+  if (nb < 1 || h < 1) return fail(PKV_ERR_SHAPE, "caches must hold at least one block and one head");
+  if (nb > INT32_MAX) return fail(PKV_ERR_SHAPE, "too many blocks");
+  // contiguous in the stated order; the stride of a dim of extent 1 is irrelevant
+  const int64_t ks[4] = {h * b * d, b * d, d, 1}, vs[4] = {h * d * b, d * b, b, 1};
+  for (int i = 0; i < 4; ++i) {
+    if (kc->shape[i] > 1 && kc->stride[i] != ks[i])
+      return fail(PKV_ERR_LAYOUT, "k_cache must be contiguous [num_blocks, H_kv, B, d]");
+    if (vc->shape[i] > 1 && vc->stride[i] != vs[i])
+      return fail(PKV_ERR_LAYOUT, "v_cache must be contiguous [num_blocks, H_kv, d, B]");
+  }
+  if (!aligned16(kc->data) || !aligned16(vc->data)) return fail(PKV_ERR_LAYOUT, "caches must be 16-byte aligned");
+  g->num_blocks = nb; g->hkv = (int32_t)h; g->block = (int32_t)b; g->dim = (int32_t)d; g->dtype = kc->dtype;
+  return PKV_OK;
+}
+
+int check_int_vector(const pkv_tensor* t, const char* name, int64_t n) {
+  int rc;
+  if ((rc = check_tensor(t, name, 1))) return rc;
+  if (t->dtype != PKV_I32) return fail(PKV_ERR_DTYPE, "%s must be int32", name);
+  if (t->shape[0] != n) return fail(PKV_ERR_SHAPE, "%s: expected %lld entries, got %lld", name, (long long)n, (long long)t->shape[0]);
+  if (n > 1 && t->stride[0] != 1) return fail(PKV_ERR_LAYOUT, "%s must be contiguous", name);
+  return PKV_OK;
+}
+
+int check_block_tables(const pkv_tensor* t, int64_t rows) {
+  int rc;
+  if ((rc = check_tensor(t, "block_tables", 2))) return rc;
+  if (t->dtype != PKV_I32) return fail(PKV_ERR_DTYPE, "block_tables must be int32");
+  if (t->shape[0] != rows) return fail(PKV_ERR_SHAPE, "block_tables has %lld rows, expected %lld", (long long)t->shape[0], (long long)rows);
+  if (t->shape[1] < 1) return fail(PKV_ERR_SHAPE, "block_tables needs at least one column");
+  if (t->shape[1] > INT32_MAX / 32) return fail(PKV_ERR_SHAPE, "block_tables too wide");
+  if ((t->shape[1] > 1 && t->stride[1] != 1) || (rows > 1 && t->stride[0] < t->shape[1]))
+    return fail(PKV_ERR_LAYOUT, "block_tables rows must be contiguous");
+  return PKV_OK;
+}
+
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+pkv::DT to_dt(int d) { return static_cast<pkv::DT>(d); }
+
+size_t decode_ws_bytes(int64_t num_seqs, int32_t hq, int32_t hkv, int32_t d, int64_t max_blocks, int32_t b,
+                       pkv::SplitPlan* plan_out) {
+  const int32_t group = hq / hkv;
+  const int32_t head_chunks = (group + 15) / 16;
+  pkv::SplitPlan plan = pkv::plan_decode_splits(num_seqs, hkv, head_chunks, max_blocks * b, device_cus());
+  if (plan_out) *plan_out = plan;
+  if (plan.num_splits <= 1) return 0;
+  return (size_t)num_seqs * hq * plan.num_splits * (size_t)(d + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_last_error(void) { return g_error.c_str(); }
+
+int pkv_append(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* slot_mapping,
+               const pkv_tensor* k_cache, const pkv_tensor* v_cache, float k_scale, float v_scale,
+               void* stream) {
+  int rc;
+  CacheGeom cg;
+  if ((rc = check_caches(k_cache, v_cache, &cg))) return rc;
+  if ((rc = check_tensor(k, "k", 3))) return rc;
+  if ((rc = check_tensor(v, "v", 3))) return rc;
+  if ((rc = check_tensor(slot_mapping, "slot_mapping", 1))) return rc;
+  const int64_t T = k->shape[0];
+  for (int i = 0; i < 3; ++i)
+    if (v->shape[i] != k->shape[i]) return fail(PKV_ERR_SHAPE, "k and v shapes differ");
+  if (k->shape[1] != cg.hkv || k->shape[2] != cg.dim)
+    return fail(PKV_ERR_SHAPE, "k/v rows are [%lld, %lld] but the cache holds [H_kv=%d, d=%d]",
+                (long long)k->shape[1], (long long)k->shape[2], cg.hkv, cg.dim);
+  if (slot_mapping->shape[0] != T) return fail(PKV_ERR_SHAPE, "slot_mapping has %lld entries for %lld tokens",
+                                               (long long)slot_mapping->shape[0], (long long)T);
+  if (slot_mapping->dtype != PKV_I32 && slot_mapping->dtype != PKV_I64)
+    return fail(PKV_ERR_DTYPE, "slot_mapping must be int32 or int64");
+  if (T > 1 && slot_mapping->stride[0] != 1) return fail(PKV_ERR_LAYOUT, "slot_mapping must be contiguous");
+  if (k->dtype != v->dtype) return fail(PKV_ERR_DTYPE, "k and v dtypes differ");
+  if (k->dtype != PKV_F32 && k->dtype != PKV_F16 && k->dtype != PKV_BF16)
+    return fail(PKV_ERR_DTYPE, "k/v rows must be f32, f16 or bf16 (got %s)", dtype_name(k->dtype));
+  if (cg.dtype == PKV_FP8_E4M3FN) {
+    if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+      return fail(PKV_ERR_SHAPE, "fp8 cache needs finite positive k_scale and v_scale");
+  } else if (k->dtype != cg.dtype) {
+    return fail(PKV_ERR_DTYPE, "rows are %s but the cache is %s (only an fp8 cache converts)",
+                dtype_name(k->dtype), dtype_name(cg.dtype));
+  }
+  if (T == 0) return ok();
+  if ((rc = check_rows(k, "k"))) return rc;
+  if ((rc = check_rows(v, "v"))) return rc;
+
+  pkv::AppendParams p{};
+  p.k = k->data; p.v = v->data;
+  p.k_s0 = k->stride[0]; p.k_s1 = k->stride[1]; p.v_s0 = v->stride[0]; p.v_s1 = v->stride[1];
+  p.slots = slot_mapping->data; p.slots_i64 = slot_mapping->dtype == PKV_I64;
+  p.k_cache = k_cache->data; p.v_cache = v_cache->data;
+  p.num_tokens = T; p.hkv = cg.hkv; p.num_blocks = (int32_t)cg.num_blocks;
+  p.k_scale = k_scale; p.v_scale = v_scale;
+  hipError_t e = pkv::launch_append(p, to_dt(k->dtype), to_dt(cg.dtype), cg.dim, cg.block, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t pkv_decode_workspace_bytes(int64_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int64_t max_blocks_per_seq, int32_t block_size) {
+  if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 ||
+      head_dim < 1 || max_blocks_per_seq < 1 || block_size < 1)
+    return 0;
+  return decode_ws_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size, nullptr);
+}
+
+int pkv_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_tensor* v_cache,
+                    const pkv_tensor* block_tables, const pkv_tensor* context_lens, float scale,
+                    float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                    const pkv_tensor* out, void* stream) {
+  int rc;
+  CacheGeom cg;
+  if ((rc = check_caches(k_cache, v_cache, &cg))) return rc;
+  if ((rc = check_tensor(q, "q", 3))) return rc;
+  if ((rc = check_tensor(out, "out", 3))) return rc;
+  const int64_t S = q->shape[0], hq = q->shape[1];
+  if (q->shape[2] != cg.dim) return fail(PKV_ERR_SHAPE, "q head_dim %lld != cache head_dim %d", (long long)q->shape[2], cg.dim);
+  for (int i = 0; i < 3; ++i)
+    if (out->shape[i] != q->shape[i]) return fail(PKV_ERR_SHAPE, "out shape differs from q");
+  if (hq < 1 || hq % cg.hkv != 0) return fail(PKV_ERR_UNSUPPORTED, "H_q=%lld is not a multiple of H_kv=%d", (long long)hq, cg.hkv);
+  if (hq > INT32_MAX || S > INT32_MAX) return fail(PKV_ERR_SHAPE, "too many sequences or heads");
+  if (out->dtype != q->dtype) return fail(PKV_ERR_DTYPE, "out dtype must equal q dtype");
+  const bool fp8 = cg.dtype == PKV_FP8_E4M3FN;
+  if (fp8) {
+    if (q->dtype != PKV_F16 && q->dtype != PKV_BF16) return fail(PKV_ERR_DTYPE, "an fp8 cache needs q in f16 or bf16");
+    if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+      return fail(PKV_ERR_SHAPE, "fp8 cache needs finite positive k_scale and v_scale");
+  } else if (q->dtype != cg.dtype) {
+    return fail(PKV_ERR_DTYPE, "q is %s but the cache is %s", dtype_name(q->dtype), dtype_name(cg.dtype));
+  }
+  if ((rc = check_block_tables(block_tables, S))) return rc;
+  if ((rc = check_int_vector(context_lens, "context_lens", S))) return rc;
+  if (!std::isfinite(scale)) return fail(PKV_ERR_SHAPE, "scale must be finite");
+  if (S == 0) return ok();
+  if ((rc = check_rows(q, "q"))) return rc;
+  if ((rc = check_rows(out, "out"))) return rc;
+
+  pkv::SplitPlan plan;
+  const size_t need = decode_ws_bytes(S, (int32_t)hq, cg.hkv, cg.dim, block_tables->shape[1], cg.block, &plan);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(PKV_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  if (need > 0 && !aligned16(workspace)) return fail(PKV_ERR_LAYOUT, "workspace must be 16-byte aligned");
+
+  pkv::DecodeParams p{};
+  p.q = q->data; p.q_s0 = q->stride[0]; p.q_s1 = q->stride[1];
+  p.k_cache = k_cache->data; p.v_cache = v_cache->data;
+  p.block_tables = reinterpret_cast<const int32_t*>(block_tables->data);
+  p.bt_s0 = block_tables->stride[0]; p.max_blocks = (int32_t)block_tables->shape[1];
+  p.context_lens = reinterpret_cast<const int32_t*>(context_lens->data);
+  p.out = out->data; p.o_s0 = out->stride[0]; p.o_s1 = out->stride[1];
+  p.num_seqs = (int32_t)S; p.hq = (int32_t)hq; p.hkv = cg.hkv; p.group = (int32_t)(hq / cg.hkv);
+  p.head_chunks = (p.group + 15) / 16; p.num_blocks = (int32_t)cg.num_blocks;
+  p.num_splits = plan.num_splits; p.split_len = plan.split_len;
+  const int64_t wgs = (int64_t)p.hkv * p.head_chunks * p.num_seqs * p.num_splits;
+  if (wgs > INT32_MAX) return fail(PKV_ERR_SHAPE, "problem too large for one launch");
+  p.total_wgs = (int32_t)wgs;
+  if (need > 0) {
+    p.ws_o = reinterpret_cast<float*>(workspace);
+    p.ws_ml = p.ws_o + (size_t)S * hq * plan.num_splits * cg.dim;
+  }
+  p.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * pkv::kLog2eHost;
+  p.v_scale = fp8 ? v_scale : 1.0f;
+  hipError_t e = pkv::launch_decode(p, to_dt(q->dtype), to_dt(cg.dtype), cg.dim, cg.block, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int pkv_suffix_prefill_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_tensor* v_cache,
+                            const pkv_tensor* block_tables, const pkv_tensor* prefix_lens,
+                            const pkv_tensor* suffix_lens, float scale, float k_scale, float v_scale,
+                            const pkv_tensor* out, void* stream) {
+  int rc;
+  CacheGeom cg;
+  if ((rc = check_caches(k_cache, v_cache, &cg))) return rc;
+  if ((rc = check_tensor(q, "q_suffix", 3))) return rc;
+  if ((rc = check_tensor(out, "out", 3))) return rc;
+  const int64_t total = q->shape[0], hq = q->shape[1];
+  if (q->shape[2] != cg.dim) return fail(PKV_ERR_SHAPE, "q_suffix head_dim %lld != cache head_dim %d", (long long)q->shape[2], cg.dim);
+  for (int i = 0; i < 3; ++i)
+    if (out->shape[i] != q->shape[i]) return fail(PKV_ERR_SHAPE, "out shape differs from q_suffix");
+  if (hq < 1 || hq % cg.hkv != 0) return fail(PKV_ERR_UNSUPPORTED, "H_q=%lld is not a multiple of H_kv=%d", (long long)hq, cg.hkv);
+  if (out->dtype != q->dtype) return fail(PKV_ERR_DTYPE, "out dtype must equal q_suffix dtype");
+  if (q->dtype != PKV_F16 && q->dtype != PKV_BF16) return fail(PKV_ERR_DTYPE, "q_suffix must be f16 or bf16 (matrix cores)");
+  const bool fp8 = cg.dtype == PKV_FP8_E4M3FN;
+  if (fp8) {
+    if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+      return fail(PKV_ERR_SHAPE, "fp8 cache needs finite positive k_scale and v_scale");
+  } else if (q->dtype != cg.dtype) {
+    return fail(PKV_ERR_DTYPE, "q_suffix is %s but the cache is %s", dtype_name(q->dtype), dtype_name(cg.dtype));
+  }
+  if ((rc = check_tensor(prefix_lens, "prefix_lens", 1))) return rc;
+  const int64_t R = prefix_lens->shape[0];
+  if ((rc = check_int_vector(prefix_lens, "prefix_lens", R))) return rc;
+  if ((rc = check_int_vector(suffix_lens, "suffix_lens", R))) return rc;
+  if ((rc = check_block_tables(block_tables, R))) return rc;
+  if (!std::isfinite(scale)) return fail(PKV_ERR_SHAPE, "scale must be finite");
+  if (total == 0 || R == 0) return ok();
+  if ((rc = check_rows(q, "q_suffix"))) return rc;
+  if ((rc = check_rows(out, "out"))) return rc;
+  if (total * (hq / cg.hkv) > INT32_MAX / 2 || R > INT32_MAX) return fail(PKV_ERR_SHAPE, "too many rows");
+
+  pkv::PrefillParams p{};
+  p.q = q->data; p.q_s0 = q->stride[0]; p.q_s1 = q->stride[1];
+  p.k_cache = k_cache->data; p.v_cache = v_cache->data;
+  p.block_tables = reinterpret_cast<const int32_t*>(block_tables->data);
+  p.bt_s0 = block_tables->stride[0]; p.max_blocks = (int32_t)block_tables->shape[1];
+  p.prefix_lens = reinterpret_cast<const int32_t*>(prefix_lens->data);
+  p.suffix_lens = reinterpret_cast<const int32_t*>(suffix_lens->data);
+  p.out = out->data; p.o_s0 = out->stride[0]; p.o_s1 = out->stride[1];
+  p.num_reqs = (int32_t)R; p.hq = (int32_t)hq; p.hkv = cg.hkv; p.group = (int32_t)(hq / cg.hkv);
+  p.num_blocks = (int32_t)cg.num_blocks; p.total_rows = total;
+  // upper bound on row tiles per KV head: sum_r ceil(S_r * G / 128) <= ceil(total * G / 128) + R
+  const int64_t tiles = (total * p.group + 127) / 128 + R;
+  if (tiles * cg.hkv > INT32_MAX) return fail(PKV_ERR_SHAPE, "problem too large for one launch");
+  p.tiles_per_head = (int32_t)tiles;
+  p.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * pkv::kLog2eHost;
+  p.v_scale = fp8 ? v_scale : 1.0f;
+  hipError_t e = pkv::launch_prefill(p, to_dt(q->dtype), to_dt(cg.dtype), cg.dim, cg.block, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

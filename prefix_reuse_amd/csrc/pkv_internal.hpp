@@ -1,0 +1,65 @@
+// Internal host/device interface of libpkv: launch parameter blocks and the
+// launchers each kernel file provides. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+enum class DT : int { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3, I32 = 4, I64 = 5 };
+
+struct AppendParams {
+  const void* k; const void* v;       // [T, Hkv, D]
+  int64_t k_s0, k_s1, v_s0, v_s1;     // element strides of token / head
+  const void* slots; int slots_i64;   // [T]
+  void* k_cache; void* v_cache;       // [NB, Hkv, B, D] / [NB, Hkv, D, B]
+  int64_t num_tokens;
+  int32_t hkv, num_blocks;
+  float k_scale, v_scale;
+};
+
+struct DecodeParams {
+  const void* q; int64_t q_s0, q_s1;  // [S, Hq, D]
+  const void* k_cache; const void* v_cache;
+  const int32_t* block_tables; int64_t bt_s0; int32_t max_blocks;
+  const int32_t* context_lens;
+  void* out; int64_t o_s0, o_s1;
+  float* ws_o;                        // [S, Hq, splits, D] unnormalised partial outputs
+  float* ws_ml;                       // [S, Hq, splits, 2] running max (log2 units) and sum
+  int32_t num_seqs, hq, hkv, group, head_chunks, num_blocks;
+  int32_t num_splits, split_len;      // split_len: tokens, multiple of 128
+  int32_t total_wgs;
+  float qk_scale_log2;                // softmax scale * k_scale * log2(e)
+  float v_scale;
+};
+
+struct PrefillParams {
+  const void* q; int64_t q_s0, q_s1;  // [total, Hq, D]
+  const void* k_cache; const void* v_cache;
+  const int32_t* block_tables; int64_t bt_s0; int32_t max_blocks;
+  const int32_t* prefix_lens; const int32_t* suffix_lens;
+  void* out; int64_t o_s0, o_s1;
+  int32_t num_reqs, hq, hkv, group, num_blocks;
+  int64_t total_rows;                 // sum_r S_r (host-known)
+  int32_t tiles_per_head;             // grid size / hkv (upper bound on tiles)
+  float qk_scale_log2;
+  float v_scale;
+};
+
+// Split selection shared by the decode launcher and the workspace-size query.
+struct SplitPlan { int32_t num_splits; int32_t split_len; };
+SplitPlan plan_decode_splits(int64_t num_seqs, int32_t hkv, int32_t head_chunks,
+                             int64_t max_ctx, int32_t num_cus);
+
+hipError_t launch_append(const AppendParams& p, DT row_dt, DT cache_dt, int head_dim,
+                         int block_size, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, DT q_dt, DT cache_dt, int head_dim,
+                         int block_size, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, DT q_dt, DT cache_dt, int head_dim,
+                          int block_size, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,161 @@
+"""Host-only checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/pkv.h declares, and rejects bad arguments with a
+status code and a message before launching anything."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import prefix_reuse_amd as pkv
+from prefix_reuse_amd import PkvTensor
+
+HEADER = Path(__file__).resolve().parent.parent / "include" / "pkv.h"
+
+F32, F16, BF16, FP8, I32, I64 = range(6)
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"pkv_append", "pkv_decode_attn", "pkv_suffix_prefill_attn", "pkv_decode_workspace_bytes",
+            "pkv_last_error", "pkv_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(pkv.lib, n), n
+
+
+def test_abi_version():
+    assert pkv.abi_version() == 1
+
+
+def T(shape, dtype, strides=None, ptr=FAKE):
+    t = PkvTensor()
+    t.data = ptr
+    t.dtype = dtype
+    t.ndim = len(shape)
+    if strides is None:
+        strides, acc = [], 1
+        for s in reversed(shape):
+            strides.insert(0, acc)
+            acc *= s
+    for i, (s, st) in enumerate(zip(shape, strides)):
+        t.shape[i] = s
+        t.stride[i] = st
+    return t
+
+
+def caches(nb=8, h=2, b=16, d=64, dt=F16):
+    return T([nb, h, b, d], dt), T([nb, h, d, b], dt)
+
+
+def R(x):
+    return ctypes.byref(x) if x is not None else None
+
+
+def decode(q, kc, vc, bt, cl, out, ws=None, ws_bytes=0, scale=0.125, ks=1.0, vs=1.0):
+    return pkv.lib.pkv_decode_attn(R(q), R(kc), R(vc), R(bt), R(cl), scale, ks, vs, ws, ws_bytes, R(out), None)
+
+
+def err():
+    return pkv.lib.pkv_last_error().decode()
+
+
+def test_decode_rejects_null_descriptor():
+    kc, vc = caches()
+    rc = decode(None, kc, vc, T([2, 4], I32), T([2], I32), T([2, 4, 64], F16))
+    assert rc == 1 and "q" in err()
+
+
+def test_decode_rejects_group_mismatch():
+    kc, vc = caches(h=3)
+    rc = decode(T([2, 4, 64], F16), kc, vc, T([2, 4], I32), T([2], I32), T([2, 4, 64], F16))
+    assert rc == 5 and "multiple" in err()
+
+
+def test_decode_rejects_dtype_mismatch():
+    kc, vc = caches(dt=BF16)
+    rc = decode(T([2, 4, 64], F16), kc, vc, T([2, 4], I32), T([2], I32), T([2, 4, 64], F16))
+    assert rc == 2
+    kc, vc = caches(dt=FP8)
+    rc = decode(T([2, 4, 64], F32), kc, vc, T([2, 4], I32), T([2], I32), T([2, 4, 64], F32))
+    assert rc == 2 and "fp8" in err()
+
+
+def test_decode_rejects_unsupported_head_dim_and_block():
+    kc, vc = caches(d=96)
+    assert decode(T([2, 4, 96], F16), kc, vc, T([2, 4], I32), T([2], I32), T([2, 4, 96], F16)) == 5
+    kc, vc = caches(b=8)
+    assert decode(T([2, 4, 64], F16), kc, vc, T([2, 4], I32), T([2], I32), T([2, 4, 64], F16)) == 5
+
+
+def test_decode_rejects_wrong_cache_layout():
+    kc, _ = caches()
+    vc_wrong = T([8, 2, 16, 64], F16)  # V given in the K layout
+    assert decode(T([2, 4, 64], F16), kc, vc_wrong, T([2, 4], I32), T([2], I32), T([2, 4, 64], F16)) == 3
+    kc_strided = T([8, 2, 16, 64], F16, strides=[4096, 2048, 64, 1])  # not contiguous
+    _, vc = caches()
+    assert decode(T([2, 4, 64], F16), kc_strided, vc, T([2, 4], I32), T([2], I32), T([2, 4, 64], F16)) == 4
+
+
+def test_decode_rejects_bad_tables_and_lengths():
+    kc, vc = caches()
+    assert decode(T([2, 4, 64], F16), kc, vc, T([2, 4], I64), T([2], I32), T([2, 4, 64], F16)) == 2
+    assert decode(T([2, 4, 64], F16), kc, vc, T([3, 4], I32), T([2], I32), T([2, 4, 64], F16)) == 3
+    assert decode(T([2, 4, 64], F16), kc, vc, T([2, 4], I32), T([2], I64), T([2, 4, 64], F16)) == 2
+
+
+def test_decode_rejects_misaligned_rows():
+    kc, vc = caches()
+    q = T([2, 4, 64], F16, ptr=FAKE + 2)
+    assert decode(q, kc, vc, T([2, 4], I32), T([2], I32), T([2, 4, 64], F16)) == 4
+
+
+def test_decode_rejects_missing_workspace_when_splitting():
+    need = pkv.decode_workspace_bytes(1, 4, 2, 64, 4096, 16)
+    assert need > 0  # one long sequence is split
+    kc, vc = caches()
+    rc = decode(T([1, 4, 64], F16), kc, vc, T([1, 4096], I32), T([1], I32), T([1, 4, 64], F16))
+    assert rc == 6 and "workspace" in err()
+
+
+def test_workspace_size_formula():
+    assert pkv.decode_workspace_bytes(0, 4, 3, 64, 4, 16) == 0  # 4 % 3 != 0
+    n = pkv.decode_workspace_bytes(1, 32, 8, 128, 3125, 32)
+    assert n % ((128 + 2) * 4 * 32) == 0
+
+
+def test_append_rejects_bad_arguments():
+    kc, vc = caches()
+    k = T([3, 2, 64], F16)
+    slots = T([3], I64)
+    f = pkv.lib.pkv_append
+    assert f(R(k), R(k), R(T([4], I64)), R(kc), R(vc), 1.0, 1.0, None) == 3
+    assert f(R(k), R(k), R(T([3], F32)), R(kc), R(vc), 1.0, 1.0, None) == 2
+    assert f(R(T([3, 2, 64], BF16)), R(T([3, 2, 64], BF16)), R(slots), R(kc), R(vc), 1.0, 1.0, None) == 2
+    k8, v8 = caches(dt=FP8)
+    assert f(R(k), R(k), R(slots), R(k8), R(v8), 0.0, 1.0, None) == 3  # scale must be > 0
+    assert f(R(T([3, 4, 64], F16)), R(T([3, 4, 64], F16)), R(slots), R(kc), R(vc), 1.0, 1.0, None) == 3
+
+
+def test_prefill_rejects_bad_arguments():
+    kc, vc = caches()
+    f = pkv.lib.pkv_suffix_prefill_attn
+    q = T([10, 4, 64], F16)
+    ok_bt, pl, sl = T([2, 4], I32), T([2], I32), T([2], I32)
+    assert f(R(T([10, 4, 64], F32)), R(kc), R(vc), R(ok_bt), R(pl), R(sl), 0.1, 1.0, 1.0, R(T([10, 4, 64], F32)), None) == 2
+    assert f(R(q), R(kc), R(vc), R(ok_bt), R(pl), R(T([3], I32)), 0.1, 1.0, 1.0, R(q), None) == 3
+    assert f(R(q), R(kc), R(vc), R(T([2, 4], I32)), R(pl), R(sl), 0.1, 1.0, 1.0, R(T([9, 4, 64], F16)), None) == 3
+    assert f(R(q), R(kc), R(vc), R(ok_bt), R(pl), R(sl), float("nan"), 1.0, 1.0, R(q), None) == 3
+
+
+def test_empty_batches_are_accepted_without_launch():
+    kc, vc = caches()
+    assert decode(T([0, 4, 64], F16), kc, vc, T([0, 4], I32), T([0], I32), T([0, 4, 64], F16)) == 0
+    f = pkv.lib.pkv_append
+    assert f(R(T([0, 2, 64], F16)), R(T([0, 2, 64], F16)), R(T([0], I64)), R(kc), R(vc), 1.0, 1.0, None) == 0

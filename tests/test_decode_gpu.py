@@ -1,0 +1,100 @@
+"""Decode parity: the HIP path against the oracle, element by element, on
+seeded inputs (tolerance 2e-3 for f32/f16/bf16 caches, 2e-2 for fp8)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import prefix_reuse_amd as pkv
+import workloads
+from _helpers import (TOL, fp8_inputs_from_pools, gpu_decode, gpu_fp8_decode, np64, oracle_decode,
+                      oracle_fp8_caches, report)
+
+pytestmark = pytest.mark.gpu
+
+# lengths around block and chunk edges: 1, B-1, B, B+1, 31/32/33, a few chunks, a ragged tail
+RAGGED = [1, 15, 16, 17, 31, 32, 33, 100, 257, 600, 1029]
+
+
+def test_config1_tiny_decode_fp32():
+    case = workloads.config1_tiny_decode()
+    run = gpu_decode(case)
+    ref = oracle_decode(case)
+    err = report("config1", np64(run.out), ref)
+    assert err <= TOL[torch.float32]
+    print(f"  fp32 informational bound 1e-5: {'met' if err <= 1e-5 else 'not met'} ({err:.2e})")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("block,dim", [(16, 64), (16, 128), (32, 64), (32, 128)])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 4), (16, 1)])
+def test_decode_ragged(dtype, block, dim, hq, hkv):
+    print(f"decode ragged dtype={dtype} B={block} d={dim} hq={hq} hkv={hkv}", flush=True)
+    case = workloads.make_decode_case(300 + dim + block + hq, RAGGED, hq, hkv, dim, block, dtype)
+    run = gpu_decode(case)
+    ref = oracle_decode(case)
+    assert report("ragged", np64(run.out), ref, dtype, TOL[dtype]) <= 1.0
+
+
+@pytest.mark.parametrize("q_dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("block,dim", [(16, 128), (32, 128), (32, 64)])
+def test_decode_fp8_ragged(q_dtype, block, dim):
+    print(f"decode fp8 q={q_dtype} B={block} d={dim}", flush=True)
+    case = workloads.make_decode_case(400 + dim + block, RAGGED, 8, 2, dim, block, torch.float32)
+    inp = fp8_inputs_from_pools(case, q_dtype)
+    run = gpu_fp8_decode(case, inp, q_dtype)
+    kc, vc = oracle_fp8_caches(case, inp)
+    ref = oracle.decode_attention(np64(case.q.to(q_dtype)), kc, vc, case.block_tables.numpy(),
+                                  case.context_lens.numpy(), case.scale, fp8=True,
+                                  k_scale=inp.k_scale, v_scale=inp.v_scale)
+    assert report("fp8", np64(run.out), ref, q_dtype, TOL["fp8"]) <= 1.0
+
+
+def test_decode_large_group_needs_two_head_chunks():
+    case = workloads.make_decode_case(77, [50, 300, 7], 40, 2, 64, 16, torch.float16)
+    run = gpu_decode(case)
+    assert report("G=20", np64(run.out), oracle_decode(case), torch.float16, TOL[torch.float16]) <= 1.0
+
+
+def test_decode_zero_length_rows_are_zero():
+    case = workloads.make_decode_case(78, [40, 1, 90], 8, 2, 128, 16, torch.bfloat16)
+    case.context_lens[1] = 0
+    case.slot_mapping[1] = -1
+    run = gpu_decode(case)
+    out = np64(run.out)
+    assert np.array_equal(out[1], np.zeros_like(out[1]))
+    ref = oracle_decode(case)
+    assert report("zero-len", out, ref, torch.bfloat16, TOL[torch.bfloat16]) <= 1.0
+
+
+def test_decode_strided_q_and_out():
+    case = workloads.make_decode_case(79, [64, 200], 8, 2, 128, 32, torch.float16)
+    kc, vc = pkv.caches_from_logical(case.k_pool, case.v_pool)
+    pkv.append(case.k_new.cuda(), case.v_new.cuda(), case.slot_mapping.cuda(), kc, vc)
+    big = torch.zeros(2, 8 * 3, 128, dtype=torch.float16, device="cuda")
+    q = big[:, ::3]  # head stride 3 rows
+    q.copy_(case.q.cuda())
+    outbuf = torch.full((2, 16, 128), 7.0, dtype=torch.float16, device="cuda")
+    out = outbuf[:, 8:]
+    pkv.decode_attn(q, kc, vc, case.block_tables.cuda(), case.context_lens.cuda(), case.scale, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(outbuf[:, :8] == 7.0)
+    assert report("strided", np64(out), oracle_decode(case), torch.float16, TOL[torch.float16]) <= 1.0
+
+
+@pytest.mark.slow
+def test_config2_llama_decode_full():
+    case = workloads.config2_llama_decode()
+    run = gpu_decode(case)
+    ref = oracle_decode(case)
+    assert report("config2", np64(run.out), ref, torch.float16, TOL[torch.float16]) <= 1.0
+
+
+@pytest.mark.slow
+def test_config3_shared_prefix_decode_full():
+    case = workloads.config3_shared_prefix_decode()
+    run = gpu_decode(case)
+    ref = oracle_decode(case)
+    assert report("config3", np64(run.out), ref, torch.bfloat16, TOL[torch.bfloat16]) <= 1.0

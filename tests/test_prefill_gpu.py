@@ -1,0 +1,98 @@
+"""Suffix-prefill parity: the HIP path against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import prefix_reuse_amd as pkv
+import workloads
+from _helpers import TOL, fp8_inputs_from_pools, gpu_prefill, nan_fp8_caches, np64, oracle_fp8_caches, oracle_prefill, report
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("block,dim", [(16, 128), (32, 128), (16, 64), (32, 64)])
+def test_prefill_ragged(dtype, block, dim):
+    print(f"prefill ragged dtype={dtype} B={block} d={dim}", flush=True)
+    prefix = [0, 4, 31, 100, 257, 0, 45]
+    suffix = [1, 1, 33, 70, 40, 130, 9]
+    case = workloads.make_prefill_case(500 + block + dim, prefix, suffix, 8, 2, dim, block, dtype)
+    run = gpu_prefill(case)
+    assert report("prefill", np64(run.out), oracle_prefill(case), dtype, TOL[dtype]) <= 1.0
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 2), (12, 4), (32, 1)])
+def test_prefill_group_sizes(hq, hkv):
+    print(f"prefill group hq={hq} hkv={hkv}", flush=True)
+    case = workloads.make_prefill_case(600 + hq + hkv, [10, 77], [50, 21], hq, hkv, 128, 16, torch.bfloat16)
+    run = gpu_prefill(case)
+    assert report("group", np64(run.out), oracle_prefill(case), torch.bfloat16, TOL[torch.bfloat16]) <= 1.0
+
+
+def test_prefill_what_day_is_it_shape():
+    # 4 cached tokens, 1 new token: the new row equals a decode of 5 tokens
+    case = workloads.make_prefill_case(601, [4], [1], 32, 8, 128, 16, torch.bfloat16)
+    run = gpu_prefill(case)
+    assert report("P4S1", np64(run.out), oracle_prefill(case), torch.bfloat16, TOL[torch.bfloat16]) <= 1.0
+
+
+def test_prefill_empty_suffix_requests_are_skipped():
+    case = workloads.make_prefill_case(602, [30, 10, 0], [0, 25, 0], 8, 2, 128, 16, torch.float16)
+    run = gpu_prefill(case)
+    assert run.out.shape[0] == 25
+    assert report("empty", np64(run.out), oracle_prefill(case), torch.float16, TOL[torch.float16]) <= 1.0
+
+
+@pytest.mark.parametrize("q_dtype", [torch.bfloat16, torch.float16])
+def test_prefill_fp8_cache(q_dtype):
+    case = workloads.make_prefill_case(603, [64, 300, 0], [40, 17, 90], 8, 2, 128, 32, torch.float32)
+    # the cached prefix and the new suffix rows are both quantized by append
+    inp = fp8_inputs_from_pools(case, q_dtype)
+    kc, vc = nan_fp8_caches(case)
+    pkv.append(inp.rows_k.cuda(), inp.rows_v.cuda(), inp.slots.cuda(), kc, vc, inp.k_scale, inp.v_scale)
+    q = case.q_suffix.to(q_dtype)
+    out = pkv.suffix_prefill_attn(q.cuda(), kc, vc, case.block_tables.cuda(), case.prefix_lens.cuda(),
+                                  case.suffix_lens.cuda(), case.scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
+    torch.cuda.synchronize()
+    ek, ev = oracle_fp8_caches(case, inp)
+    ref = oracle.suffix_prefill_attention(np64(q), ek, ev, case.block_tables.numpy(), case.prefix_lens.numpy(),
+                                          case.suffix_lens.numpy(), case.scale, fp8=True,
+                                          k_scale=inp.k_scale, v_scale=inp.v_scale)
+    assert report("prefill-fp8", np64(out), ref, q_dtype, TOL["fp8"]) <= 1.0
+
+
+@pytest.mark.slow
+def test_config4_suffix_prefill_sampled_rows():
+    case = workloads.config4_suffix_prefill()
+    run = gpu_prefill(case)
+    out = np64(run.out)
+    assert np.isfinite(out).all()
+    # every request's first two and last two rows, plus a seeded sample
+    rng = np.random.default_rng(4)
+    rows = set()
+    for r in range(16):
+        rows |= {100 * r, 100 * r + 1, 100 * r + 98, 100 * r + 99}
+    rows |= set(rng.choice(1600, 40, replace=False).tolist())
+    rows = sorted(rows)
+    ref = oracle_prefill(case, rows=rows)
+    assert report("config4", out[rows], ref[rows], torch.bfloat16, TOL[torch.bfloat16]) <= 1.0
+
+
+@pytest.mark.slow
+def test_config4_reuse_equals_full_recompute_on_gpu():
+    """The 2,000-token request with 1,900 cached gives the same 100 rows as
+    prefilling all 2,000 (prefix reuse does not change the output)."""
+    full = workloads.make_prefill_case(1004, [0], [2000], 32, 8, 128, 16, torch.bfloat16)
+    run_full = gpu_prefill(full)
+    kc, vc = run_full.k_cache, run_full.v_cache
+    q_tail = full.q_suffix[1900:].cuda()
+    out = pkv.suffix_prefill_attn(q_tail, kc, vc, full.block_tables.cuda(), torch.tensor([1900], dtype=torch.int32).cuda(),
+                                  torch.tensor([100], dtype=torch.int32).cuda(), full.scale)
+    torch.cuda.synchronize()
+    # suffix-only rows against the full-prefill rows (two GPU results) ...
+    assert report("reuse-vs-full", np64(out), np64(run_full.out[1900:]), torch.bfloat16, TOL[torch.bfloat16]) <= 1.0
+    # ... and both against the oracle on a sample of rows
+    rows = [0, 1, 50, 98, 99]
+    ref = oracle_prefill(full, rows=[1900 + r for r in rows])
+    assert report("reuse-oracle", np64(out)[rows], ref[[1900 + r for r in rows]], torch.bfloat16, TOL[torch.bfloat16]) <= 1.0
