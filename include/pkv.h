@@ -112,11 +112,13 @@ int pkv_append(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* slot_
 
 /*
  * pkv_decode_workspace_bytes — bytes of device workspace pkv_decode_attn needs
- * for this problem size on the CURRENT device (the split count it picks
- * depends on the device's compute-unit count; the environment variable
- * PKV_DECODE_SPLIT_LEN, a positive multiple of 128, forces the context split
- * length in tokens for both calls). Returns 0 on invalid sizes and when no
- * split is needed.
+ * on the CURRENT device: per-wave partial results for sequences that several
+ * waves share, (waves_per_head + num_seqs) * H_q * (head_dim + 2) floats, plus
+ * two ints per sequence. waves_per_head = 12 * (compute units) / (H_kv *
+ * ceil(G / 16)), at least 1; the environment variable PKV_DECODE_WAVES (a
+ * positive integer) replaces the 12 * (compute units) total for both calls.
+ * max_blocks_per_seq and block_size do not change the size (kept for
+ * callers that size by the full problem). Returns 0 on invalid sizes.
  */
 size_t pkv_decode_workspace_bytes(int64_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int64_t max_blocks_per_seq,
@@ -141,8 +143,9 @@ size_t pkv_decode_workspace_bytes(int64_t num_seqs, int32_t num_q_heads, int32_t
  *  k_scale,      dequantization scales of an fp8 cache (ignored otherwise).
  *  v_scale
  *  workspace     device buffer of at least pkv_decode_workspace_bytes(...)
- *                bytes (the caller allocates it; it holds per-split partial
- *                results). May be NULL only if that function returns 0.
+ *                bytes, 16-byte aligned (the caller allocates it; it holds
+ *                partial results). No initial contents are needed; calls
+ *                that share one workspace must be ordered on one stream.
  *  out           [num_seqs, H_q, d], same dtype as q; last dim contiguous.
  * Results are bitwise deterministic and depend only on logical positions, so
  * permuting physical blocks or aliasing identical blocks between sequences

@@ -148,14 +148,15 @@ int device_cus() {
 
 pkv::DT to_dt(int d) { return static_cast<pkv::DT>(d); }
 
-size_t decode_ws_bytes(int64_t num_seqs, int32_t hq, int32_t hkv, int32_t d, int64_t max_blocks, int32_t b,
-                       pkv::SplitPlan* plan_out) {
+// Workspace: partial results [waves_per_head + S][Hq][D + 2] floats, then
+// [S][2] ints of per-sequence partition info.
+size_t decode_ws_bytes(int64_t num_seqs, int32_t hq, int32_t hkv, int32_t d, pkv::DecodePlan* plan_out) {
   const int32_t group = hq / hkv;
   const int32_t head_chunks = (group + 15) / 16;
-  pkv::SplitPlan plan = pkv::plan_decode_splits(num_seqs, hkv, head_chunks, max_blocks * b, device_cus());
+  pkv::DecodePlan plan = pkv::plan_decode(num_seqs, hkv, head_chunks, device_cus());
   if (plan_out) *plan_out = plan;
-  if (plan.num_splits <= 1) return 0;
-  return (size_t)num_seqs * hq * plan.num_splits * (size_t)(d + 2) * sizeof(float);
+  const size_t slots = (size_t)plan.waves_per_head + (size_t)num_seqs;
+  return slots * hq * (size_t)(d + 2) * sizeof(float) + (size_t)num_seqs * 2 * sizeof(int32_t);
 }
 
 }  // namespace
@@ -217,7 +218,9 @@ size_t pkv_decode_workspace_bytes(int64_t num_seqs, int32_t num_q_heads, int32_t
   if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 ||
       head_dim < 1 || max_blocks_per_seq < 1 || block_size < 1)
     return 0;
-  return decode_ws_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size, nullptr);
+  (void)max_blocks_per_seq;
+  (void)block_size;
+  return decode_ws_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, nullptr);
 }
 
 int pkv_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_tensor* v_cache,
@@ -251,11 +254,11 @@ int pkv_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_te
   if ((rc = check_rows(q, "q"))) return rc;
   if ((rc = check_rows(out, "out"))) return rc;
 
-  pkv::SplitPlan plan;
-  const size_t need = decode_ws_bytes(S, (int32_t)hq, cg.hkv, cg.dim, block_tables->shape[1], cg.block, &plan);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+  pkv::DecodePlan plan;
+  const size_t need = decode_ws_bytes(S, (int32_t)hq, cg.hkv, cg.dim, &plan);
+  if (workspace == nullptr || workspace_bytes < need)
     return fail(PKV_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need, workspace_bytes);
-  if (need > 0 && !aligned16(workspace)) return fail(PKV_ERR_LAYOUT, "workspace must be 16-byte aligned");
+  if (!aligned16(workspace)) return fail(PKV_ERR_LAYOUT, "workspace must be 16-byte aligned");
 
   pkv::DecodeParams p{};
   p.q = q->data; p.q_s0 = q->stride[0]; p.q_s1 = q->stride[1];
@@ -266,14 +269,12 @@ int pkv_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_te
   p.out = out->data; p.o_s0 = out->stride[0]; p.o_s1 = out->stride[1];
   p.num_seqs = (int32_t)S; p.hq = (int32_t)hq; p.hkv = cg.hkv; p.group = (int32_t)(hq / cg.hkv);
   p.head_chunks = (p.group + 15) / 16; p.num_blocks = (int32_t)cg.num_blocks;
-  p.num_splits = plan.num_splits; p.split_len = plan.split_len;
-  const int64_t wgs = (int64_t)p.hkv * p.head_chunks * p.num_seqs * p.num_splits;
-  if (wgs > INT32_MAX) return fail(PKV_ERR_SHAPE, "problem too large for one launch");
-  p.total_wgs = (int32_t)wgs;
-  if (need > 0) {
-    p.ws_o = reinterpret_cast<float*>(workspace);
-    p.ws_ml = p.ws_o + (size_t)S * hq * plan.num_splits * cg.dim;
-  }
+  p.waves_per_head = plan.waves_per_head;
+  p.total_wgs = plan.total_waves;
+  const size_t slots = (size_t)plan.waves_per_head + (size_t)S;
+  p.ws_o = reinterpret_cast<float*>(workspace);
+  p.ws_ml = p.ws_o + slots * hq * cg.dim;
+  p.seq_info = reinterpret_cast<int32_t*>(p.ws_ml + slots * hq * 2);
   p.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * pkv::kLog2eHost;
   p.v_scale = fp8 ? v_scale : 1.0f;
   hipError_t e = pkv::launch_decode(p, to_dt(q->dtype), to_dt(cg.dtype), cg.dim, cg.block, (hipStream_t)stream);

@@ -7,11 +7,19 @@
 // block table, with query head h reading KV head h / G.
 //
 // Design (decode is bound by reading the KV cache from HBM):
-//  * One work-group of 4 waves per (KV head, sequence, context split). The
-//    whole GQA group (up to 16 query heads) is served from one read of K and V.
-//  * Each wave walks 32-token chunks of its split (chunk k goes to wave k % 4).
-//    Both products run on the matrix cores with operands loaded straight from
-//    global memory in 16-byte pieces:
+//  * Balanced, persistent partition. Every 32-token chunk of every sequence
+//    is one unit of work; for each KV head (and group of up to 16 query heads)
+//    a fixed number of one-wave work-groups - as many as the chip holds at
+//    once - each take an equal, contiguous range of the chunks in sequence
+//    order. A wave keeps its softmax state across the chunks of a sequence and
+//    writes a result only when it leaves the sequence: the final output if it
+//    saw the whole sequence, else an unnormalised partial (O, m, l) that a
+//    small combine kernel merges in wave order. Lengths that differ by 8x
+//    therefore cost nothing in balance, and no wave idles on an empty split.
+//  * The whole GQA group (up to 16 query heads) is served from one read of K
+//    and V. Both products run on the matrix cores with operands loaded
+//    straight from global memory in 16-byte pieces, all of a chunk's loads
+//    issued before the first product:
 //      S^T[token][head] = K[token][:] . Q[head][:]     (A = K rows, B = Q^T)
 //      O^T[dim][head]  += V^T[dim][token] . P^T[token][head]
 //    The second product needs V with tokens contiguous, which is why the V
@@ -21,10 +29,8 @@
 //    and exactly 8 contiguous tokens of a V^T row.
 //  * Online softmax in base 2 with the scale folded into one multiplier; the
 //    running max is made uniform across the wave with two lane exchanges.
-//  * The 4 waves merge through LDS in a fixed order. With one split the result
-//    is written directly; otherwise an unnormalised partial (O, m, l) goes to
-//    the workspace and a combine kernel merges splits in a fixed order, so the
-//    result is bitwise deterministic and depends only on logical positions.
+//  * Results are bitwise deterministic; arithmetic order depends only on
+//    logical positions and on the partition, never on timing.
 #include "pkv_device.hpp"
 #include "pkv_internal.hpp"
 
@@ -35,8 +41,6 @@
 namespace pkv {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kChunk = 32;
 
 template <typename TQ, typename TC, int D>
@@ -143,90 +147,167 @@ __device__ __forceinline__ f32x4 score_tile(const ChunkRegs<TC, D>& r, int a, co
   return s;
 }
 
+// Chunk bookkeeping of the balanced partition: every 32-token chunk of every
+// sequence, in sequence order, is one unit of work; wave w of a KV head takes
+// units [w * per_wave, (w + 1) * per_wave).
+struct Partition {
+  int total;     // chunks of all sequences
+  int per_wave;  // ceil(total / waves per head)
+};
+
+__device__ __forceinline__ int ctx_of(const DecodeParams& p, int s, int cap) {
+  int c = p.context_lens[s];
+  return c < 0 ? 0 : (c > cap ? cap : c);
+}
+
+// Wave-wide inclusive scan of one value per lane.
+__device__ __forceinline__ int wave_scan(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
 template <typename TQ, typename TC, int D, int BLK>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64, 3) void decode_kernel(DecodeParams p) {
   typedef typename QFrag<TQ, TC, D>::T QT;
   typedef ChunkRegs<TC, D> R;
   constexpr int QS = QFrag<TQ, TC, D>::kSteps;
   constexpr int NT = D / 16;  // output dim tiles
-  constexpr int LDS_ROW = D + 4;
   constexpr bool kSplitP = std::is_same<TQ, bf16_t>::value;  // bf16 P as hi + lo
 
-  extern __shared__ float smem[];
-  const int nh_max = min(16, p.group);
-  float* s_acc = smem;                                  // [kWaves][nh_max][LDS_ROW]
-  float* s_m = smem + kWaves * nh_max * LDS_ROW;        // [kWaves][nh_max]
-  float* s_l = s_m + kWaves * nh_max;                   // [kWaves][nh_max]
-
   const int logical = xcd_remap(blockIdx.x, p.total_wgs);
-  const int split = logical % p.num_splits;
-  const int rest = logical / p.num_splits;
-  const int seq = rest % p.num_seqs;
-  const int hkc = rest / p.num_seqs;  // kv head * head_chunks + chunk
+  const int hkc = logical / p.waves_per_head;  // kv head * head_chunks + chunk
+  const int w = logical % p.waves_per_head;
   const int hk = hkc / p.head_chunks;
   const int hchunk = hkc % p.head_chunks;
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // uniform: scalar table reads
-  const int lane = tid % 64;
+  const int lane = threadIdx.x;
   const int g = lane / 16, c16 = lane % 16;
-
   const int cap = p.max_blocks * BLK;
-  int ctx = p.context_lens[seq];
-  ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
-  const int t0 = split * p.split_len;
-  const int nh = min(16, p.group - hchunk * 16);  // valid query heads in this work-group
+  const int nh = min(16, p.group - hchunk * 16);
 
-  if (t0 >= ctx) {
-    if (p.num_splits == 1) {  // empty context: zero output rows
-      for (int idx = tid; idx < nh * D; idx += kThreads) {
-        int h = idx / D, d = idx % D;
-        int qh = hk * p.group + hchunk * 16 + h;
-        reinterpret_cast<TQ*>(p.out)[seq * p.o_s0 + qh * p.o_s1 + d] = from_f32<TQ>(0.f);
-      }
-    }
-    return;
+  // ---- partition: total chunks, this wave's range, its first sequence ----
+  int total = 0;
+  for (int b = 0; b < p.num_seqs; b += 64) {
+    const int s = b + lane;
+    int ch = s < p.num_seqs ? (ctx_of(p, s, cap) + kChunk - 1) / kChunk : 0;
+    total += __shfl(wave_scan(ch, lane), 63);
   }
-  const int t1 = min(t0 + p.split_len, ctx);
+  total = __builtin_amdgcn_readfirstlane(total);
+  if (total == 0) return;
+  const int per_wave = (total + p.waves_per_head - 1) / p.waves_per_head;
+  const int c0 = w * per_wave;
+  const int c1 = min(c0 + per_wave, total);
+  // per-sequence partition info, written once for the combine kernel
+  if (logical == 0) {
+    int run = 0;
+    for (int b = 0; b < p.num_seqs; b += 64) {
+      const int s = b + lane;
+      int ch = s < p.num_seqs ? (ctx_of(p, s, cap) + kChunk - 1) / kChunk : 0;
+      const int incl = run + wave_scan(ch, lane);
+      const int first = incl - ch;
+      if (s < p.num_seqs) {
+        p.seq_info[2 * s] = ch > 0 ? first / per_wave : 0;                                // first wave
+        p.seq_info[2 * s + 1] = ch > 0 ? (incl - 1) / per_wave - first / per_wave + 1 : 0;  // waves
+      }
+      run = __shfl(incl, 63);
+    }
+  }
+  if (c0 >= c1) return;
+  // first sequence of the range: the one whose chunks contain c0
+  int s_cur = 0, s_first_chunk = 0;
+  {
+    int run = 0;
+    for (int b = 0; b < p.num_seqs; b += 64) {
+      const int s = b + lane;
+      int ch = s < p.num_seqs ? (ctx_of(p, s, cap) + kChunk - 1) / kChunk : 0;
+      const int incl = run + wave_scan(ch, lane);
+      const unsigned long long hit = __ballot(s < p.num_seqs && incl > c0);
+      if (hit) {
+        const int l0 = __builtin_ctzll(hit);
+        s_cur = b + l0;
+        s_first_chunk = __shfl(incl - ch, l0);
+        break;
+      }
+      run = __shfl(incl, 63);
+    }
+  }
+  s_cur = __builtin_amdgcn_readfirstlane(s_cur);
+  s_first_chunk = __builtin_amdgcn_readfirstlane(s_first_chunk);
 
-  // ---- Q fragments (zero for padding heads) ----
-  const bool hvalid = c16 < nh;
-  const int qh_lane = hk * p.group + hchunk * 16 + (hvalid ? c16 : 0);
-  const TQ* qrow = reinterpret_cast<const TQ*>(p.q) + seq * p.q_s0 + qh_lane * p.q_s1;
-  QT qf[QS];
-  load_q<TQ, TC, D>(qf, qrow, hvalid, g);
-
-  const int32_t* bt = p.block_tables + seq * p.bt_s0;
   const TC* kbase = reinterpret_cast<const TC*>(p.k_cache);
   const TC* vbase = reinterpret_cast<const TC*>(p.v_cache);
+  const bool hvalid = c16 < nh;
+  const int qh_lane = hk * p.group + hchunk * 16 + (hvalid ? c16 : 0);
 
+  QT qf[QS];
   f32x4 acc[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run, l_run;
+  int ctx = ctx_of(p, s_cur, cap);
+  int tb = (c0 - s_first_chunk) * kChunk;
+  const int32_t* bt = p.block_tables + (int64_t)s_cur * p.bt_s0;
 
-  auto blocks_of = [&](int tb, int& b0, int& b1) {
+  auto start_seq = [&]() {
+    load_q<TQ, TC, D>(qf, reinterpret_cast<const TQ*>(p.q) + s_cur * p.q_s0 + qh_lane * p.q_s1, hvalid, g);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
+  };
+
+  // write this wave's result for s_cur: final output if it saw the whole
+  // sequence, else an unnormalised partial in slot (w + s_cur)
+  auto finish_seq = [&](bool whole) {
+    float l = l_run + __shfl_xor(l_run, 16);
+    l += __shfl_xor(l, 32);
+    if (!hvalid) return;
+    const int qh = hk * p.group + hchunk * 16 + c16;
+    if (whole) {
+      const float inv = p.v_scale / l;
+      TQ* o = reinterpret_cast<TQ*>(p.out) + s_cur * p.o_s0 + qh * p.o_s1;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        typedef __attribute__((__vector_size__(4 * sizeof(TQ)))) TQ TQx4;
+        TQx4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = from_f32<TQ>(acc[n][i] * inv);
+        *reinterpret_cast<TQx4*>(o + 16 * n + 4 * g) = v;
+      }
+    } else {
+      const int64_t row = (int64_t)(w + s_cur) * p.hq + qh;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(p.ws_o + row * D + 16 * n + 4 * g) = acc[n];
+      if (g == 0) { p.ws_ml[row * 2] = m_run; p.ws_ml[row * 2 + 1] = l; }
+    }
+  };
+
+  start_seq();
+  int seq_start = s_first_chunk;  // global index of s_cur's first chunk
+  for (int c = c0; c < c1; ++c) {
+    // ---- load the chunk ----
     const int jb = tb / BLK;
-    b0 = bt[jb];
-    b1 = b0;
+    int b0 = bt[jb], b1 = b0;
     if constexpr (BLK == 16) {
-      if ((jb + 1) * BLK < t1) b1 = bt[jb + 1];  // only entries that hold live tokens
+      if ((jb + 1) * BLK < ctx) b1 = bt[jb + 1];  // only entries that hold live tokens
     }
     b0 = min(max(b0, 0), p.num_blocks - 1);
     b1 = min(max(b1, 0), p.num_blocks - 1);
-  };
+    R r;
+    load_chunk<TC, D, BLK>(r, kbase, vbase, b0, b1, hk, p.hkv, c16, g);
 
-  auto compute = [&](const R& r, int tb) {
+    // ---- scores S^T for 32 tokens: two 16-token tiles ----
     float sc[8];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
-      f32x4 s = score_tile<TQ, TC, D>(r, a, qf);
+      f32x4 sv = score_tile<TQ, TC, D>(r, a, qf);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[4 * a + i] = s[i] * p.qk_scale_log2;
+      for (int i = 0; i < 4; ++i) sc[4 * a + i] = sv[i] * p.qk_scale_log2;
     }
-    // lane (g, c16) holds chunk tokens tb + 8g + j, j = 0..7, of head c16
-    const int nvalid = min(max(t1 - (tb + 8 * g), 0), 8);
-    const bool tail = tb + kChunk > t1;
+    // lane (g, c16) holds tokens tb + 8g + j, j = 0..7, of head c16
+    const int nvalid = min(max(ctx - (tb + 8 * g), 0), 8);
+    const bool tail = tb + kChunk > ctx;
     if (tail) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) sc[j] = j < nvalid ? sc[j] : -INFINITY;
@@ -286,104 +367,53 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         if constexpr (kSplitP) acc[n] = mfma16x16x32(vf[n], plo, acc[n]);
       }
     }
-  };
 
-  // ---- two-stage register pipeline over this wave's chunks ----
-  // The next chunk's loads are always issued (past the end they re-read the
-  // current chunk's addresses), so every iteration has the same number of
-  // loads in flight and the waits before each product cover only its own data.
-  R bufA, bufB;
-  int tb = t0 + wave * kChunk;
-  constexpr int kStride = kWaves * kChunk;
-  if (tb < t1) {
-    int b0, b1;
-    blocks_of(tb, b0, b1);
-    load_chunk<TC, D, BLK>(bufA, kbase, vbase, b0, b1, hk, p.hkv, c16, g);
-    for (;;) {
-      int tn = tb + kStride;
-      bool more = tn < t1;
-      int n0 = b0, n1 = b1;
-      if (more) blocks_of(tn, n0, n1);
-      load_chunk<TC, D, BLK>(bufB, kbase, vbase, n0, n1, hk, p.hkv, c16, g);
-      compute(bufA, tb);
-      if (!more) break;
-      tb = tn;
-      b0 = n0; b1 = n1;
-      tn = tb + kStride;
-      more = tn < t1;
-      if (more) blocks_of(tn, n0, n1);
-      load_chunk<TC, D, BLK>(bufA, kbase, vbase, n0, n1, hk, p.hkv, c16, g);
-      compute(bufB, tb);
-      if (!more) break;
-      tb = tn;
-      b0 = n0; b1 = n1;
-    }
-  }
-
-  // ---- merge the lane groups' partial sums, then the 4 waves through LDS ----
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  if (c16 < nh) {
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-      *reinterpret_cast<f32x4*>(&s_acc[(wave * nh_max + c16) * LDS_ROW + 16 * n + 4 * g]) = acc[n];
-    if (g == 0) { s_m[wave * nh_max + c16] = m_run; s_l[wave * nh_max + c16] = l_run; }
-  }
-  __syncthreads();
-
-  for (int idx = tid; idx < nh * D; idx += kThreads) {
-    const int h = idx / D, d = idx % D;
-    float M = s_m[h];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w * nh_max + h]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = exp2f(s_m[w * nh_max + h] - M);  // 0 for a wave that saw no token
-      L += s_l[w * nh_max + h] * f;
-      O += s_acc[(w * nh_max + h) * LDS_ROW + d] * f;
-    }
-    const int qh = hk * p.group + hchunk * 16 + h;
-    if (p.num_splits == 1) {
-      reinterpret_cast<TQ*>(p.out)[seq * p.o_s0 + qh * p.o_s1 + d] = from_f32<TQ>(O / L * p.v_scale);
-    } else {
-      const int64_t row = ((int64_t)seq * p.hq + qh) * p.num_splits + split;
-      p.ws_o[row * D + d] = O;
-      if (d == 0) { p.ws_ml[row * 2] = M; p.ws_ml[row * 2 + 1] = L; }
+    // ---- advance ----
+    tb += kChunk;
+    if (tb >= ctx || c + 1 == c1) {
+      const int nch = (ctx + kChunk - 1) / kChunk;
+      finish_seq(seq_start >= c0 && seq_start + nch <= c1);
+      if (c + 1 == c1) break;
+      seq_start += nch;
+      do {  // next non-empty sequence
+        ++s_cur;
+        ctx = ctx_of(p, s_cur, cap);
+      } while (ctx == 0);
+      tb = 0;
+      bt = p.block_tables + (int64_t)s_cur * p.bt_s0;
+      start_seq();
     }
   }
 }
 
-// Merge the splits of one (sequence, query head) in split order.
+// Merge the partials of one (sequence, query head) in wave order; sequences
+// that one wave covered entirely already hold their output.
 template <typename TQ, int D, int BLK>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
   const int seq = blockIdx.x / p.hq, qh = blockIdx.x % p.hq;
   const int d = threadIdx.x;
   const int cap = p.max_blocks * BLK;
-  int ctx = p.context_lens[seq];
-  ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
-  const int n = (ctx + p.split_len - 1) / p.split_len;
   TQ* out = reinterpret_cast<TQ*>(p.out) + seq * p.o_s0 + qh * p.o_s1;
-  if (n == 0) { out[d] = from_f32<TQ>(0.f); return; }
-  const int64_t row0 = ((int64_t)seq * p.hq + qh) * p.num_splits;
+  if (ctx_of(p, seq, cap) == 0) { out[d] = from_f32<TQ>(0.f); return; }
+  const int first = p.seq_info[2 * seq], n = p.seq_info[2 * seq + 1];
+  if (n <= 1) return;
   float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, p.ws_ml[(row0 + i) * 2]);
+  for (int i = 0; i < n; ++i) M = fmaxf(M, p.ws_ml[((int64_t)(first + i + seq) * p.hq + qh) * 2]);
   float L = 0.f, O = 0.f;
   for (int i = 0; i < n; ++i) {
-    const float f = exp2f(p.ws_ml[(row0 + i) * 2] - M);
-    L += p.ws_ml[(row0 + i) * 2 + 1] * f;
-    O += p.ws_o[(row0 + i) * D + d] * f;
+    const int64_t row = (int64_t)(first + i + seq) * p.hq + qh;
+    const float f = exp2f(p.ws_ml[row * 2] - M);
+    L += p.ws_ml[row * 2 + 1] * f;
+    O += p.ws_o[row * D + d] * f;
   }
   out[d] = from_f32<TQ>(O / L * p.v_scale);
 }
 
 template <typename TQ, typename TC, int D, int BLK>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
-  const int nh_max = p.group < 16 ? p.group : 16;
-  const size_t lds = (size_t)kWaves * nh_max * ((D + 4) + 2) * sizeof(float);
-  hipLaunchKernelGGL((decode_kernel<TQ, TC, D, BLK>), dim3(p.total_wgs), dim3(kThreads), lds, stream, p);
+  hipLaunchKernelGGL((decode_kernel<TQ, TC, D, BLK>), dim3(p.total_wgs), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.num_splits == 1) return e;
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<TQ, D, BLK>), dim3(p.num_seqs * p.hq), dim3(D), 0, stream, p);
   return hipGetLastError();
 }
@@ -399,30 +429,20 @@ hipError_t launch_shape(const DecodeParams& p, int d, int b, hipStream_t s) {
 
 }  // namespace
 
-SplitPlan plan_decode_splits(int64_t num_seqs, int32_t hkv, int32_t head_chunks, int64_t max_ctx,
-                             int32_t num_cus) {
-  // Aim for about 8 work-groups per compute unit in total; never split below
-  // 256 tokens; split lengths are whole multiples of 4 waves x 32 tokens.
-  // PKV_DECODE_SPLIT_LEN (a positive multiple of 128) forces the split length.
-  if (const char* env = getenv("PKV_DECODE_SPLIT_LEN")) {
+DecodePlan plan_decode(int64_t num_seqs, int32_t hkv, int32_t head_chunks, int32_t num_cus) {
+  // One wave per work-group, about 12 waves per compute unit in total (what
+  // fits at once), split evenly over the (KV head, head chunk) pairs.
+  // PKV_DECODE_WAVES (a positive integer) forces the total.
+  int64_t waves = 12LL * (num_cus > 0 ? num_cus : 256);
+  if (const char* env = getenv("PKV_DECODE_WAVES")) {
     const long forced = atol(env);
-    if (forced >= 128 && forced % 128 == 0) {
-      int64_t splits = (max_ctx + forced - 1) / forced;
-      return SplitPlan{(int32_t)(splits < 1 ? 1 : splits), (int32_t)forced};
-    }
+    if (forced > 0) waves = forced;
   }
-  const int64_t units = num_seqs * hkv * head_chunks;
-  const int64_t target = 8LL * (num_cus > 0 ? num_cus : 256);
-  int64_t splits = units > 0 ? (target + units - 1) / units : 1;
-  const int64_t max_splits = (max_ctx + 255) / 256;
-  if (splits > max_splits) splits = max_splits;
-  if (splits < 1) splits = 1;
-  int64_t len = (max_ctx + splits - 1) / splits;
-  len = ((len + 127) / 128) * 128;
-  if (len < 128) len = 128;
-  splits = (max_ctx + len - 1) / len;
-  if (splits < 1) splits = 1;
-  return SplitPlan{(int32_t)splits, (int32_t)len};
+  const int64_t units = (int64_t)hkv * head_chunks;
+  int64_t per_head = waves / units;
+  if (per_head < 1) per_head = 1;
+  (void)num_seqs;
+  return DecodePlan{(int32_t)per_head, (int32_t)(per_head * units)};
 }
 
 hipError_t launch_decode(const DecodeParams& p, DT q_dt, DT cache_dt, int d, int b, hipStream_t s) {

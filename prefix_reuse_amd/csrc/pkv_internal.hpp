@@ -28,11 +28,12 @@ struct DecodeParams {
   const int32_t* block_tables; int64_t bt_s0; int32_t max_blocks;
   const int32_t* context_lens;
   void* out; int64_t o_s0, o_s1;
-  float* ws_o;                        // [S, Hq, splits, D] unnormalised partial outputs
-  float* ws_ml;                       // [S, Hq, splits, 2] running max (log2 units) and sum
+  float* ws_o;                        // [waves_per_head + S, Hq, D] unnormalised partial outputs
+  float* ws_ml;                       // [waves_per_head + S, Hq, 2] running max (log2 units) and sum
+  int32_t* seq_info;                  // [S, 2] first wave and number of waves of each sequence
   int32_t num_seqs, hq, hkv, group, head_chunks, num_blocks;
-  int32_t num_splits, split_len;      // split_len: tokens, multiple of 128
-  int32_t total_wgs;
+  int32_t waves_per_head;             // waves sharing the chunks of one (KV head, head chunk)
+  int32_t total_wgs;                  // one wave per work-group
   float qk_scale_log2;                // softmax scale * k_scale * log2(e)
   float v_scale;
 };
@@ -50,10 +51,9 @@ struct PrefillParams {
   float v_scale;
 };
 
-// Split selection shared by the decode launcher and the workspace-size query.
-struct SplitPlan { int32_t num_splits; int32_t split_len; };
-SplitPlan plan_decode_splits(int64_t num_seqs, int32_t hkv, int32_t head_chunks,
-                             int64_t max_ctx, int32_t num_cus);
+// Decode launch plan shared by the launcher and the workspace-size query.
+struct DecodePlan { int32_t waves_per_head; int32_t total_waves; };
+DecodePlan plan_decode(int64_t num_seqs, int32_t hkv, int32_t head_chunks, int32_t num_cus);
 
 hipError_t launch_append(const AppendParams& p, DT row_dt, DT cache_dt, int head_dim,
                          int block_size, hipStream_t stream);

@@ -116,18 +116,24 @@ def test_decode_rejects_misaligned_rows():
     assert decode(q, kc, vc, T([2, 4], I32), T([2], I32), T([2, 4, 64], F16)) == 4
 
 
-def test_decode_rejects_missing_workspace_when_splitting():
+def test_decode_rejects_missing_workspace():
     need = pkv.decode_workspace_bytes(1, 4, 2, 64, 4096, 16)
-    assert need > 0  # one long sequence is split
+    assert need > 0
     kc, vc = caches()
     rc = decode(T([1, 4, 64], F16), kc, vc, T([1, 4096], I32), T([1], I32), T([1, 4, 64], F16))
     assert rc == 6 and "workspace" in err()
+    rc = decode(T([1, 4, 64], F16), kc, vc, T([1, 4096], I32), T([1], I32), T([1, 4, 64], F16),
+                ws=FAKE, ws_bytes=need - 1)
+    assert rc == 6
 
 
-def test_workspace_size_formula():
+def test_workspace_size_formula(monkeypatch):
     assert pkv.decode_workspace_bytes(0, 4, 3, 64, 4, 16) == 0  # 4 % 3 != 0
-    n = pkv.decode_workspace_bytes(1, 32, 8, 128, 3125, 32)
-    assert n % ((128 + 2) * 4 * 32) == 0
+    monkeypatch.setenv("PKV_DECODE_WAVES", "64")
+    # 64 waves over 8 KV heads -> 8 per head; slots = 8 + S; plus 2 ints per sequence
+    assert pkv.decode_workspace_bytes(5, 32, 8, 128, 3125, 32) == (8 + 5) * 32 * 130 * 4 + 5 * 8
+    # 40 query heads over 2 KV heads: G = 20 needs 2 head chunks -> 4 units, 16 waves each
+    assert pkv.decode_workspace_bytes(3, 40, 2, 64, 10, 16) == (16 + 3) * 40 * 66 * 4 + 3 * 8
 
 
 def test_append_rejects_bad_arguments():
