@@ -114,9 +114,9 @@ int pkv_append(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* slot_
  * pkv_decode_workspace_bytes — bytes of device workspace pkv_decode_attn needs
  * on the CURRENT device: per-wave partial results for sequences that several
  * waves share, (waves_per_head + num_seqs) * H_q * (head_dim + 2) floats, plus
- * two ints per sequence. waves_per_head = 12 * (compute units) / (H_kv *
+ * two ints per sequence. waves_per_head = 8 * (compute units) / (H_kv *
  * ceil(G / 16)), at least 1; the environment variable PKV_DECODE_WAVES (a
- * positive integer) replaces the 12 * (compute units) total for both calls.
+ * positive integer) replaces the 8 * (compute units) total for both calls.
  * max_blocks_per_seq and block_size do not change the size (kept for
  * callers that size by the full problem). Returns 0 on invalid sizes.
  */

@@ -168,7 +168,8 @@ def decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     need = decode_workspace_bytes(q.shape[0], q.shape[1], k_cache.shape[1], q.shape[2],
                                   block_tables.shape[1], block_size)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        # zero-filled once: the kernel's arrival counters start at 0 and are left at 0
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if (need and workspace is not None) else None
     ws_bytes = workspace.numel() * workspace.element_size() if (need and workspace is not None) else 0
     dq, dkc, dvc, dbt, dcl, do = map(_desc, (q, k_cache, v_cache, block_tables, context_lens, out))

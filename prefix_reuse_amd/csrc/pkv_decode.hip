@@ -386,27 +386,47 @@ __global__ __launch_bounds__(64, 3) void decode_kernel(DecodeParams p) {
   }
 }
 
-// Merge the partials of one (sequence, query head) in wave order; sequences
-// that one wave covered entirely already hold their output.
+// Merge the partials of the sequences that several waves shared, in wave
+// order. One work-group per (sequence, group of 8 query heads); each thread
+// owns 4 consecutive dims of one head. Sequences that one wave covered
+// entirely already hold their output; empty sequences get zero rows here.
+constexpr int kCombineHeads = 8;
+
 template <typename TQ, int D, int BLK>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
-  const int seq = blockIdx.x / p.hq, qh = blockIdx.x % p.hq;
-  const int d = threadIdx.x;
+__global__ __launch_bounds__(kCombineHeads * D / 4) void decode_combine_kernel(DecodeParams p) {
+  const int groups = (p.hq + kCombineHeads - 1) / kCombineHeads;
+  const int seq = blockIdx.x / groups;
+  const int qh = (blockIdx.x % groups) * kCombineHeads + threadIdx.x / (D / 4);
+  const int d0 = (threadIdx.x % (D / 4)) * 4;
+  if (qh >= p.hq) return;
   const int cap = p.max_blocks * BLK;
-  TQ* out = reinterpret_cast<TQ*>(p.out) + seq * p.o_s0 + qh * p.o_s1;
-  if (ctx_of(p, seq, cap) == 0) { out[d] = from_f32<TQ>(0.f); return; }
+  TQ* out = reinterpret_cast<TQ*>(p.out) + seq * p.o_s0 + qh * p.o_s1 + d0;
+  typedef __attribute__((__vector_size__(4 * sizeof(TQ)))) TQ TQx4;
+  if (ctx_of(p, seq, cap) == 0) {
+    TQx4 z;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[i] = from_f32<TQ>(0.f);
+    *reinterpret_cast<TQx4*>(out) = z;
+    return;
+  }
   const int first = p.seq_info[2 * seq], n = p.seq_info[2 * seq + 1];
   if (n <= 1) return;
+  const int64_t row0 = (int64_t)(first + seq) * p.hq + qh;  // slot of wave `first`
   float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, p.ws_ml[((int64_t)(first + i + seq) * p.hq + qh) * 2]);
-  float L = 0.f, O = 0.f;
+  for (int i = 0; i < n; ++i) M = fmaxf(M, p.ws_ml[(row0 + (int64_t)i * p.hq) * 2]);
+  float L = 0.f;
+  f32x4 O = {0.f, 0.f, 0.f, 0.f};
   for (int i = 0; i < n; ++i) {
-    const int64_t row = (int64_t)(first + i + seq) * p.hq + qh;
+    const int64_t row = row0 + (int64_t)i * p.hq;
     const float f = exp2f(p.ws_ml[row * 2] - M);
     L += p.ws_ml[row * 2 + 1] * f;
-    O += p.ws_o[row * D + d] * f;
+    O += *reinterpret_cast<const f32x4*>(p.ws_o + row * D + d0) * f;
   }
-  out[d] = from_f32<TQ>(O / L * p.v_scale);
+  const float inv = p.v_scale / L;
+  TQx4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = from_f32<TQ>(O[i] * inv);
+  *reinterpret_cast<TQx4*>(out) = v;
 }
 
 template <typename TQ, typename TC, int D, int BLK>
@@ -414,7 +434,9 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((decode_kernel<TQ, TC, D, BLK>), dim3(p.total_wgs), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<TQ, D, BLK>), dim3(p.num_seqs * p.hq), dim3(D), 0, stream, p);
+  const int groups = (p.hq + kCombineHeads - 1) / kCombineHeads;
+  hipLaunchKernelGGL((decode_combine_kernel<TQ, D, BLK>), dim3(p.num_seqs * groups), dim3(kCombineHeads * D / 4), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -430,10 +452,11 @@ hipError_t launch_shape(const DecodeParams& p, int d, int b, hipStream_t s) {
 }  // namespace
 
 DecodePlan plan_decode(int64_t num_seqs, int32_t hkv, int32_t head_chunks, int32_t num_cus) {
-  // One wave per work-group, about 12 waves per compute unit in total (what
-  // fits at once), split evenly over the (KV head, head chunk) pairs.
+  // One wave per work-group, 8 waves per compute unit in total (2 per SIMD:
+  // enough loads in flight to keep HBM busy, few enough that each wave's run
+  // is long), split evenly over the (KV head, head chunk) pairs.
   // PKV_DECODE_WAVES (a positive integer) forces the total.
-  int64_t waves = 12LL * (num_cus > 0 ? num_cus : 256);
+  int64_t waves = 8LL * (num_cus > 0 ? num_cus : 256);
   if (const char* env = getenv("PKV_DECODE_WAVES")) {
     const long forced = atol(env);
     if (forced > 0) waves = forced;
