@@ -15,21 +15,24 @@
 //    registers.
 //  * Keys are consumed 64 per stage, double buffered in LDS (the next stage's
 //    loads are in flight while this one is computed; one barrier per stage).
-//    16-bit K goes from global memory straight to LDS (global_load_lds); V is
-//    staged through registers, converted to f16 and zeroed past the end. Both
-//    LDS tiles are XOR-swizzled so that the matrix-core operand reads are free
-//    of bank conflicts.
+//    16-bit K and V go from global memory straight to LDS (global_load_lds);
+//    fp8 tiles are staged through registers and converted. Values of keys past
+//    the end are zeroed in LDS (they meet P = 0, and 0 * NaN would be NaN).
+//    Both LDS tiles are XOR-swizzled so that the matrix-core operand reads are
+//    free of bank conflicts. Block ids come from scalar loads two stages ahead.
 //  * Per wave and 32-key sub-tile, on v_mfma_f32_32x32x16:
-//      S^T[key][row] = K[key][:] . Q[row][:]           (bf16 or f16)
-//      O^T[dim][row] += V^T[dim][keys] . P^T[keys][row]  (f16)
+//      S^T[key][row] = K[key][:] . Q[row][:]
+//      O^T[dim][row] += V^T[dim][keys] . P^T[keys][row]
 //    K rows are read in a permuted order so that each lane ends up holding 16
 //    consecutive keys of one row: the B operand of the PV product.
-//  * P and V enter the PV product as f16 (11-bit mantissa): P is in [0, 2^8]
-//    (lazy rescaling below), and a bf16 V is scaled by 2^-8 on the way in
-//    (exact for |v| in [2^-6, 65504 * 2^8]; below that the absolute error is
-//    at most 2^-17; beyond it the value saturates), the 2^8 is put back at the
-//    end. bf16 P would carry only 8 bits, too few for 2e-3 on short contexts.
-//  * Online softmax in base 2 with the scale folded in; the running max moves
+//  * Precision of P in the PV product: with f16 operands P is rounded to f16
+//    (11 bits, P is in [0, 2^8] thanks to the lazy rescale below). With bf16
+//    operands P would carry only 8 bits - too few for 2e-3 on short contexts -
+//    so P goes in as bf16(P) + bf16(P - bf16(P)): two products on the matrix
+//    cores, which have room to spare, instead of converting V on the vector
+//    units, which do not. fp8 V is converted exactly to f16 while staging.
+//  * Online softmax in base 2 with the scale folded into one FMA per score and
+//    the raw v_exp_f32 (results below 2^-126 flush to 0); the running max moves
 //    only when a row's max grows by more than 2^8 (lazy rescale), so the
 //    output accumulators are rarely rescaled. The causal mask is applied only
 //    on key tiles that reach past the wave's first token.
@@ -70,134 +73,124 @@ __device__ __forceinline__ int v_off(int d, int piece) {  // piece in [0, 8)
 template <typename TQ, typename TC>
 struct Types {
   static constexpr bool kFp8 = std::is_same<TC, uint8_t>::value;
-  static constexpr bool kKDirect = !kFp8;                           // K lands in LDS as stored
-  // V always goes through registers: keys past the end must become 0 (they
-  // meet P = 0, and 0 * NaN would be NaN), which a direct-to-LDS load cannot do.
-  static constexpr bool kVDirect = false;
-  static constexpr bool kVScaled = std::is_same<TC, bf16_t>::value;
+  static constexpr bool kDirect = !kFp8;  // 16-bit tiles land in LDS as stored
+  // PV operand type: the cache's own 16-bit type, f16 for an fp8 cache
+  typedef typename std::conditional<kFp8, f16_t, TC>::type VOp;
+  static constexpr bool kSplitP = std::is_same<VOp, bf16_t>::value;
 };
 
 template <typename TQ, typename TC, int D, int BLK>
 struct Stage {
   typedef Types<TQ, TC> T;
-  // register staging: V pieces of 8 keys (16-bit: 16 B, fp8: 8 B); fp8 K pieces of 16 dims
-  static constexpr int kVPieces = T::kVDirect ? 0 : D * (kStage / 8) / kThreads;
-  static constexpr int kKPieces = T::kKDirect ? 0 : kStage * (D / 16) / kThreads;
-  typedef typename std::conditional<T::kFp8, u32x2, u32x4>::type VPiece;
-  VPiece vr[kVPieces > 0 ? kVPieces : 1];
-  u32x4 kr[kKPieces > 0 ? kKPieces : 1];
+  typedef typename T::VOp VOp;
+  static constexpr int kBlocks = kStage / BLK;  // blocks per stage
+  // fp8 register staging: K pieces of 16 dims (16 codes), V pieces of 8 keys
+  // (8 codes); an empty struct for 16-bit tiles, which go straight to LDS
+  static constexpr int kKPieces = kStage * (D / 16) / kThreads;
+  static constexpr int kVPieces = D * (kStage / 8) / kThreads;
+  struct Fp8Regs {
+    u32x4 kr[kKPieces];
+    u32x2 vr[kVPieces];
+  };
+  struct NoRegs {};
+  typedef typename std::conditional<T::kDirect, NoRegs, Fp8Regs>::type Regs;
 
-  __device__ __forceinline__ static int block_of(const int32_t* bt, int pos, int max_blocks, int num_blocks) {
-    int jb = pos / BLK;
-    jb = jb < max_blocks ? jb : max_blocks - 1;
-    const int b = bt[jb];
-    return min(max(b, 0), num_blocks - 1);
+  // Block ids of one stage, kept in four plain ints (arrays or structs here
+  // end up in LDS or scratch). Loaded with scalar loads: pointer and index
+  // are uniform; entries past the end repeat the last block with a live key.
+  __device__ __forceinline__ static void load_ids(int& b0, int& b1, int& b2, int& b3, const int32_t* bt, int st,
+                                                  int kv_len, int max_blocks, int num_blocks) {
+    static_assert(kBlocks == 2 || kBlocks == 4, "16- or 32-token blocks");
+    const int last = min((kv_len - 1) / BLK, max_blocks - 1);
+    auto id = [&](int i) {
+      const int jb = min(st * kBlocks + i, last);
+      return min(max(bt[jb], 0), num_blocks - 1);
+    };
+    b0 = id(0);
+    b1 = id(1);
+    b2 = kBlocks == 4 ? id(2) : 0;
+    b3 = kBlocks == 4 ? id(3) : 0;
+  }
+  __device__ __forceinline__ static int pick(int b0, int b1, int b2, int b3, int i) {  // i in [0, kBlocks)
+    if constexpr (kBlocks == 2) return i == 0 ? b0 : b1;
+    else return i < 2 ? (i == 0 ? b0 : b1) : (i == 2 ? b2 : b3);
   }
 
-  // Issue this thread's loads of stage `st` (keys st*kStage ..): direct-to-LDS
-  // pieces go to (k_lds, v_lds); register pieces to kr / vr.
-  __device__ __forceinline__ void issue(const TC* kbase, const TC* vbase, const int32_t* bt, int hk, int hkv,
-                                        int num_blocks, int max_blocks, int st, int kv_len, TQ* k_lds,
-                                        f16_t* v_lds, int wave, int lane) {
+  // Issue this thread's loads of stage `st` (keys st*kStage ..) with the
+  // stage's block ids: direct-to-LDS for 16-bit tiles, registers for fp8.
+  __device__ __forceinline__ static void issue(Regs& rg, const TC* kbase, const TC* vbase, int b0, int b1, int b2,
+                                               int b3, int hk, int hkv, int st, int kv_len, TQ* k_lds, VOp* v_lds,
+                                               int wave, int lane) {
     const int key0 = st * kStage;
     const int64_t tile = (int64_t)BLK * D;
-    if constexpr (T::kKDirect) {
-      // 1 KB per instruction, lane-linear: rows of D*2 bytes
+    if constexpr (T::kDirect) {
+      // K: 1 KB per instruction, lane-linear, rows of D*2 bytes
       constexpr int kInst = kStage * D * 2 / 1024;
       constexpr int kRowsPerInst = 1024 / (D * 2);
       constexpr int kLanesPerRow = 64 / kRowsPerInst;
 #pragma unroll
       for (int i = 0; i < kInst / kWaves; ++i) {
         const int j = wave * (kInst / kWaves) + i;
-        const int row = j * kRowsPerInst + lane / kLanesPerRow;
+        int row = j * kRowsPerInst + lane / kLanesPerRow;
         const int piece = (lane % kLanesPerRow) ^ k_swz<D>(row);
-        int pos = key0 + row;
-        pos = pos < kv_len ? pos : kv_len - 1;  // past the end: any valid row (masked later)
-        const int blk = block_of(bt, pos, max_blocks, num_blocks);
-        const TC* src = kbase + ((int64_t)blk * hkv + hk) * tile + (int64_t)(pos % BLK) * D + piece * 8;
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                         (lds_void*)(k_lds + j * 512), 16, 0, 0);
+        if (key0 + row >= kv_len) row = kv_len - 1 - key0 >= 0 ? kv_len - 1 - key0 : 0;  // any live row
+        const TC* src = kbase + ((int64_t)pick(b0, b1, b2, b3, row / BLK) * hkv + hk) * tile + (int64_t)(row % BLK) * D + piece * 8;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (lds_void*)(k_lds + j * 512), 16, 0, 0);
       }
-    } else {
+      // V^T: 1 KB per instruction = 8 rows of 64 keys
+      constexpr int kVInst = D * kStage * 2 / 1024;
 #pragma unroll
-      for (int i = 0; i < kKPieces; ++i) {  // fp8: 16 codes = dims 16q .. 16q+15 of one key
-        const int pi = lane + 64 * (wave + kWaves * i);
-        const int row = pi / (D / 16), q = pi % (D / 16);
-        const int pos = key0 + row;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (pos < kv_len) {
-          const int blk = block_of(bt, pos, max_blocks, num_blocks);
-          w = load_u32x4(kbase + ((int64_t)blk * hkv + hk) * tile + (int64_t)(pos % BLK) * D + q * 16);
-        }
-        kr[i] = w;
-      }
-    }
-    if constexpr (T::kVDirect) {
-      // 1 KB per instruction = 8 V^T rows of 64 keys (f16)
-      constexpr int kInst = D * kStage * 2 / 1024;
-#pragma unroll
-      for (int i = 0; i < kInst / kWaves; ++i) {
-        const int j = wave * (kInst / kWaves) + i;
+      for (int i = 0; i < kVInst / kWaves; ++i) {
+        const int j = wave * (kVInst / kWaves) + i;
         const int d = j * 8 + lane / 8;
         const int piece = (lane % 8) ^ ((d >> 1) & 7);
-        int pos = key0 + piece * 8;
-        pos = pos < kv_len ? pos : ((kv_len - 1) / 8) * 8;  // past the end: any valid piece
-        const int blk = block_of(bt, pos, max_blocks, num_blocks);
-        const TC* src = vbase + ((int64_t)blk * hkv + hk) * tile + (int64_t)d * BLK + (pos % BLK);
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                         (lds_void*)(v_lds + j * 512), 16, 0, 0);
+        const int k8 = piece * 8;  // first key of the piece within the stage
+        const TC* src = vbase + ((int64_t)pick(b0, b1, b2, b3, k8 / BLK) * hkv + hk) * tile + (int64_t)d * BLK + (k8 % BLK);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (lds_void*)(v_lds + j * 512), 16, 0, 0);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < kVPieces; ++i) {
+      for (int i = 0; i < kKPieces; ++i) {  // 16 codes = dims 16q .. 16q+15 of one key
+        const int pi = lane + 64 * (wave + kWaves * i);
+        const int row = pi / (D / 16), q = pi % (D / 16);
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (key0 + row < kv_len)
+          w = load_u32x4(kbase + ((int64_t)pick(b0, b1, b2, b3, row / BLK) * hkv + hk) * tile + (int64_t)(row % BLK) * D + q * 16);
+        rg.kr[i] = w;
+      }
+#pragma unroll
+      for (int i = 0; i < kVPieces; ++i) {  // 8 codes = keys 8p .. 8p+7 of one dim
         const int pi = lane + 64 * (wave + kWaves * i);
         const int d = pi / (kStage / 8), piece = pi % (kStage / 8);
-        const int pos = key0 + piece * 8;
-        VPiece w = {};
-        if (pos < kv_len) {
-          const int blk = block_of(bt, pos, max_blocks, num_blocks);
-          w = *reinterpret_cast<const VPiece*>(vbase + ((int64_t)blk * hkv + hk) * tile + (int64_t)d * BLK + (pos % BLK));
-        }
-        vr[i] = w;
+        u32x2 w = {0u, 0u};
+        if (key0 + piece * 8 < kv_len)
+          w = load_u32x2(vbase + ((int64_t)pick(b0, b1, b2, b3, piece * 8 / BLK) * hkv + hk) * tile + (int64_t)d * BLK + (piece * 8) % BLK);
+        rg.vr[i] = w;
       }
     }
   }
 
-  // Convert and write the register-staged pieces of stage `st` into LDS.
-  __device__ __forceinline__ void commit(int st, int kv_len, TQ* k_lds, f16_t* v_lds, int wave, int lane) {
-    const int key0 = st * kStage;
-    if constexpr (!T::kKDirect) {
+  // fp8: convert the register-staged pieces of stage `st` and write them to LDS.
+  __device__ __forceinline__ static void commit(Regs& rg, int st, int kv_len, TQ* k_lds, VOp* v_lds, int wave,
+                                                int lane) {
+    if constexpr (!T::kDirect) {
       typedef typename Frag<TQ>::type F;
 #pragma unroll
       for (int i = 0; i < kKPieces; ++i) {
         const int pi = lane + 64 * (wave + kWaves * i);
         const int row = pi / (D / 16), q = pi % (D / 16);
-        u32x2 lo = {kr[i][0], kr[i][1]}, hi = {kr[i][2], kr[i][3]};
+        u32x2 lo = {rg.kr[i][0], rg.kr[i][1]}, hi = {rg.kr[i][2], rg.kr[i][3]};
         *reinterpret_cast<F*>(k_lds + k_off<D>(row, 2 * q)) = fp8x8_to<TQ>(lo);
         *reinterpret_cast<F*>(k_lds + k_off<D>(row, 2 * q + 1)) = fp8x8_to<TQ>(hi);
       }
-    }
-    if constexpr (!T::kVDirect) {
+      const int key0 = st * kStage;
 #pragma unroll
       for (int i = 0; i < kVPieces; ++i) {
         const int pi = lane + 64 * (wave + kWaves * i);
         const int d = pi / (kStage / 8), piece = pi % (kStage / 8);
+        f16x8 f = fp8x8_to<f16_t>(rg.vr[i]);  // exact: every e4m3fn value is an f16 value
         const int pos = key0 + piece * 8;
-        f16x8 f;
-        if constexpr (T::kFp8) {
-          f = fp8x8_to<f16_t>(vr[i]);  // exact: every e4m3fn value is an f16 value
-        } else if constexpr (!T::kVScaled) {
-          f = __builtin_bit_cast(f16x8, vr[i]);  // f16 cache: as stored
-        } else {                       // bf16 -> f16 with the 2^-8 range scaling, saturating
-          const bf16x8 b = __builtin_bit_cast(bf16x8, vr[i]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float x = (float)b[e] * 0.00390625f;
-            x = fminf(fmaxf(x, -65504.f), 65504.f);
-            f[e] = (f16_t)x;
-          }
-        }
-        if (pos + 8 > kv_len) {  // keys past the end meet P = 0; 0 * NaN would be NaN
+        if (pos + 8 > kv_len) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) f[e] = pos + e < kv_len ? f[e] : (f16_t)0.f;
         }
@@ -205,17 +198,33 @@ struct Stage {
       }
     }
   }
+
+  // 16-bit tiles: after the stage has landed, zero V of keys >= kv_len (the
+  // direct loads brought whatever those cache slots hold). Call with all
+  // threads of the work-group; only the stage holding kv_len has such keys.
+  __device__ __forceinline__ static void zero_tail(int st, int kv_len, VOp* v_lds, int tid) {
+    const int key0 = st * kStage;
+    const int first = kv_len - key0;  // first dead key within the stage
+    const int dead = kStage - first;
+    for (int idx = tid; idx < D * dead; idx += kThreads) {
+      const int d = idx / dead, k = first + idx % dead;
+      v_lds[v_off(d, k / 8) + (k % 8)] = (VOp)0.f;
+    }
+  }
 };
 
 template <typename TQ, typename TC, int D, int BLK>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   typedef Types<TQ, TC> T;
+  typedef typename T::VOp VOp;
   typedef typename Frag<TQ>::type F;
+  typedef typename Frag<VOp>::type FV;
+  typedef Stage<TQ, TC, D, BLK> STG;
   constexpr int QS = D / 16;  // k-steps of the score product
   constexpr int NT = D / 32;  // dim tiles of the output
   constexpr int kKElems = kStage * D, kVElems = D * kStage;
   __shared__ __attribute__((aligned(16))) TQ k_lds_all[2 * kKElems];
-  __shared__ __attribute__((aligned(16))) f16_t v_lds_all[2 * kVElems];
+  __shared__ __attribute__((aligned(16))) VOp v_lds_all[2 * kVElems];
 
   // ---- which (KV head, request, row tile) ----
   const int logical = xcd_remap(blockIdx.x, p.hkv * p.tiles_per_head);
@@ -281,29 +290,43 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 
   const TC* kbase = reinterpret_cast<const TC*>(p.k_cache);
   const TC* vbase = reinterpret_cast<const TC*>(p.v_cache);
-  Stage<TQ, TC, D, BLK> stg;
+  typename STG::Regs regs;
+  const bool tail_stage_exists = nst > 0 && kv_len < nst * kStage;
 
+  int a0 = 0, a1 = 0, a2 = 0, a3 = 0;  // block ids of stage st+1
+  int n0 = 0, n1 = 0, n2 = 0, n3 = 0;  // block ids of stage st+2
   if (nst > 0) {
-    stg.issue(kbase, vbase, bt, hk, p.hkv, p.num_blocks, p.max_blocks, 0, kv_len, k_lds_all, v_lds_all, wave, lane);
-    stg.commit(0, kv_len, k_lds_all, v_lds_all, wave, lane);
+    int z0, z1, z2, z3;
+    STG::load_ids(z0, z1, z2, z3, bt, 0, kv_len, p.max_blocks, p.num_blocks);
+    STG::issue(regs, kbase, vbase, z0, z1, z2, z3, hk, p.hkv, 0, kv_len, k_lds_all, v_lds_all, wave, lane);
+    STG::commit(regs, 0, kv_len, k_lds_all, v_lds_all, wave, lane);
+    STG::load_ids(a0, a1, a2, a3, bt, 1, kv_len, p.max_blocks, p.num_blocks);
   }
   __builtin_amdgcn_s_waitcnt(0);  // direct-to-LDS loads of stage 0 have landed
   __syncthreads();
+  if constexpr (T::kDirect) {
+    if (tail_stage_exists && nst == 1) {
+      STG::zero_tail(0, kv_len, v_lds_all, tid);
+      __syncthreads();
+    }
+  }
 
   for (int st = 0; st < nst; ++st) {
     const int buf = st & 1;
     TQ* k_lds = k_lds_all + buf * kKElems;
-    f16_t* v_lds = v_lds_all + buf * kVElems;
+    VOp* v_lds = v_lds_all + buf * kVElems;
     TQ* k_nxt = k_lds_all + (buf ^ 1) * kKElems;
-    f16_t* v_nxt = v_lds_all + (buf ^ 1) * kVElems;
-    if (st + 1 < nst)
-      stg.issue(kbase, vbase, bt, hk, p.hkv, p.num_blocks, p.max_blocks, st + 1, kv_len, k_nxt, v_nxt, wave, lane);
+    VOp* v_nxt = v_lds_all + (buf ^ 1) * kVElems;
+    if (st + 1 < nst) {
+      STG::issue(regs, kbase, vbase, a0, a1, a2, a3, hk, p.hkv, st + 1, kv_len, k_nxt, v_nxt, wave, lane);
+      STG::load_ids(n0, n1, n2, n3, bt, st + 2, kv_len, p.max_blocks, p.num_blocks);
+    }
 
 #pragma unroll
     for (int t = 0; t < kStage / 32; ++t) {
       const int key0 = st * kStage + 32 * t;  // first key of the sub-tile
       if (key0 < keys_w) {                    // uniform per wave
-        // scores: element i = key key0 + 16*h0 + i, row c32
+        // scores: element i = key key0 + 16*h0 + i, row c32 (unscaled)
         f32x16 s = {};
         const int krow = 32 * t + krow_perm;
 #pragma unroll
@@ -311,23 +334,20 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
           const F kf = *reinterpret_cast<const F*>(k_lds + k_off<D>(krow, 2 * c + h0));
           s = mfma32x32x16(kf, qf[c], s);
         }
-        float sc[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sc[i] = s[i] * p.qk_scale_log2;
         if (key0 + 32 > full_keys_w) {
           const int kb = key0 + 16 * h0;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sc[i] = (kb + i <= lim && kb + i < kv_len) ? sc[i] : -INFINITY;
+          for (int i = 0; i < 16; ++i) s[i] = (kb + i <= lim && kb + i < kv_len) ? s[i] : -INFINITY;
         }
-        float cmax = sc[0];
+        float cmax = s[0];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) cmax = fmaxf(cmax, sc[i]);
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+        for (int i = 1; i < 16; ++i) cmax = fmaxf(cmax, s[i]);
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 32)) * p.qk_scale_log2;  // scale > 0: max commutes
         // lazy rescale: move the running max only when it grows by more than 2^kLazy
         const bool grow = cmax > m_run + kLazy;
         if (__any(grow)) {
           const float m_new = grow ? cmax : m_run;
-          const float alpha = exp2f(m_run - m_new);  // 1 for rows that keep their max
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 for rows that keep their max
           m_run = m_new;
           l_run *= alpha;
 #pragma unroll
@@ -336,30 +356,53 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
         float pr[16];
         float psum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { pr[i] = exp2f(sc[i] - m_run); psum += pr[i]; }
+        for (int i = 0; i < 16; ++i) {
+          pr[i] = __builtin_amdgcn_exp2f(fmaf(s[i], p.qk_scale_log2, -m_run));
+          psum += pr[i];
+        }
         l_run += psum;
-        const f16x8 p0 = pack8<f16_t>(pr), p1 = pack8<f16_t>(pr + 8);
+        const FV p0 = pack8<VOp>(pr), p1 = pack8<VOp>(pr + 8);
+        FV p0lo, p1lo;
+        if constexpr (T::kSplitP) {
+          float lo[16];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) { lo[i] = pr[i] - (float)p0[i]; lo[8 + i] = pr[8 + i] - (float)p1[i]; }
+          p0lo = pack8<VOp>(lo);
+          p1lo = pack8<VOp>(lo + 8);
+        }
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           const int d = 32 * n + c32;
-          const f16x8 v0 = *reinterpret_cast<const f16x8*>(v_lds + v_off(d, 4 * t + 2 * h0));
-          const f16x8 v1 = *reinterpret_cast<const f16x8*>(v_lds + v_off(d, 4 * t + 2 * h0 + 1));
+          const FV v0 = *reinterpret_cast<const FV*>(v_lds + v_off(d, 4 * t + 2 * h0));
+          const FV v1 = *reinterpret_cast<const FV*>(v_lds + v_off(d, 4 * t + 2 * h0 + 1));
           acc[n] = mfma32x32x16(v0, p0, acc[n]);
           acc[n] = mfma32x32x16(v1, p1, acc[n]);
+          if constexpr (T::kSplitP) {
+            acc[n] = mfma32x32x16(v0, p0lo, acc[n]);
+            acc[n] = mfma32x32x16(v1, p1lo, acc[n]);
+          }
         }
       }
     }
 
-    if (st + 1 < nst) stg.commit(st + 1, kv_len, k_nxt, v_nxt, wave, lane);
+    if (st + 1 < nst) {
+      STG::commit(regs, st + 1, kv_len, k_nxt, v_nxt, wave, lane);
+      a0 = n0; a1 = n1; a2 = n2; a3 = n3;
+    }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's direct-to-LDS loads of the next stage have landed
     __syncthreads();
+    if constexpr (T::kDirect) {
+      if (tail_stage_exists && st + 2 == nst) {  // the next stage holds kv_len: clear dead values
+        STG::zero_tail(st + 1, kv_len, v_nxt, tid);
+        __syncthreads();
+      }
+    }
   }
 
   // ---- epilogue: O = O^T / l; element i of acc[n] is dim 32n + 8(i/4) + 4h0 + i%4 ----
   l_run += __shfl_xor(l_run, 32);
   if (rvalid) {
-    const float vback = T::kVScaled ? 256.f : 1.f;
-    const float inv = p.v_scale * vback / l_run;
+    const float inv = p.v_scale / l_run;
     TQ* orow = reinterpret_cast<TQ*>(p.out) + (int64_t)(row_base + tok) * p.o_s0 + (int64_t)qh * p.o_s1;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
