@@ -159,6 +159,68 @@ def cpu_baseline(case, min_seconds=10.0, max_seconds=30.0) -> dict:
     }
 
 
+def ingest_profile(name: str, trace_dir: str, fetch_dir: str, write_dir: str, kernel_regex: str,
+                   command: str) -> None:
+    """Summarise rocprofv3 csv output (a kernel-trace --stats run and two
+    --pmc runs, FETCH_SIZE then WRITE_SIZE) into profiles/<name>.md and
+    profiles/<name>_traffic.json. Counters are calibrated by the 1 GiB device
+    copy that `--only` runs end with: factor = true bytes / counter bytes."""
+    import csv
+    import re
+
+    rx = re.compile(kernel_regex)
+
+    def find(d, suffix):
+        hits = sorted(Path(d).rglob(f"*{suffix}"))
+        if not hits:
+            raise FileNotFoundError(f"no *{suffix} under {d}")
+        return hits[0]
+
+    stats = list(csv.DictReader(open(find(trace_dir, "kernel_stats.csv"))))
+    lines = [f"# {name}", "", "rocprofv3 summaries (MI355X, gfx950). Commands, run from /tmp with TMPDIR=/tmp:", "",
+             "```", command, "```", "", "## Kernel trace (--kernel-trace --stats)", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    total_avg_ns = 0.0
+    for r in stats:
+        short = r["Name"][:110]
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
+                     f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} |")
+        if rx.search(r["Name"]):
+            total_avg_ns += float(r["AverageNs"])
+    counters = {}
+    for label, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = list(csv.DictReader(open(find(d, "counter_collection.csv"))))
+        copy = [r for r in rows if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) >= 65536]
+        copy_kib = float(copy[-1]["Counter_Value"]) if copy else float("nan")
+        factor = (1 << 20) / copy_kib  # the copy moves 1 GiB = 2^20 KiB each way
+        per = {}
+        for r in rows:
+            if rx.search(r["Kernel_Name"]):
+                per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        counters[label] = (factor, copy_kib, {k: sum(v) / len(v) for k, v in per.items()})
+    lines += ["", "## HBM traffic (--pmc, one counter per run)", "",
+              "Calibration: the same counter over a plain 1 GiB device-to-device copy.", "",
+              "| counter | copy reads as KiB | factor | kernel | KiB per dispatch (raw) | MB per dispatch (calibrated) |",
+              "|---|---|---|---|---|---|"]
+    total_bytes = 0.0
+    parts = {}
+    for label, (factor, copy_kib, per) in counters.items():
+        for k, v in per.items():
+            mb = v * factor * 1024 / 1e6
+            total_bytes += v * factor * 1024
+            parts[f"{label}:{k[:60]}"] = round(v * factor * 1024)
+            lines.append(f"| {label} | {copy_kib:.0f} | {factor:.3f} | `{k[:60]}` | {v:.0f} | {mb:.2f} |")
+    lines += ["", f"Sum over the matched kernels: average duration {total_avg_ns/1e3:.2f} us per launch, "
+              f"HBM traffic {total_bytes/1e6:.2f} MB per launch.", ""]
+    (ROOT / "profiles").mkdir(exist_ok=True)
+    (ROOT / "profiles" / f"{name}.md").write_text("\n".join(lines))
+    rec = {"name": name, "kernel_regex": kernel_regex, "sources_hash": sources_hash(KERNEL_SOURCES),
+           "avg_launch_us": round(total_avg_ns / 1e3, 3), "bytes_per_launch": round(total_bytes),
+           "parts": parts, "command": command}
+    (ROOT / "profiles" / f"{name}_traffic.json").write_text(json.dumps(rec, indent=1) + "\n")
+    print(f"wrote profiles/{name}.md and profiles/{name}_traffic.json")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,7 +230,13 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
                     help="run only this kernel's launches (for profiler runs)")
+    ap.add_argument("--ingest-profile", nargs=5, metavar=("NAME", "TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "KERNEL_REGEX"),
+                    help="summarise rocprofv3 csv output into profiles/ (no GPU needed)")
+    ap.add_argument("--profile-command", default="", help="command text recorded with --ingest-profile")
     args = ap.parse_args()
+    if args.ingest_profile:
+        ingest_profile(*args.ingest_profile, command=args.profile_command)
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
