@@ -14,6 +14,9 @@ Printed as one JSON line:
              match the current kernel sources (else null)
   suffix_prefill  the same for the suffix-prefill workload (16 requests x
              1,900 cached + 100 new tokens, bf16): TFLOP/s against bf16 MFMA peak
+  long_context_fp8  8 sequences x 100,000 tokens x 32 layers with an fp8
+             e4m3fn cache: append + decode for every layer per step, GB/s of
+             KV read, and one layer's decode call against the HBM peak
   cpu_baseline    the CPU oracle timed on this host on the same decode workload
 
 Inputs are synthetic (seeded N(0,1)), resident in HBM before timing starts.
@@ -104,6 +107,56 @@ def prefill_setup(torch, pkv, workloads, dev):
     }
     t["out"] = torch.empty_like(t["q"])
     return t
+
+
+def long_context_setup(torch, pkv, workloads, dev, num_layers=32):
+    """Per-layer fp8 caches of the long-context workload, every token quantized
+    through pkv_append from N(0,1) rows drawn on the device (scale = amax/448
+    per layer for K and for V)."""
+    import numpy as np
+
+    case = workloads.config5_long_context_fp8(num_layers=num_layers)
+    n = case.context_len
+    layers = []
+    for layer in range(num_layers):
+        kc, vc = pkv.empty_caches(case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim,
+                                  torch.float8_e4m3fn, dev)
+        kc.view(torch.uint8).fill_(workloads.fp8_nan_code)
+        vc.view(torch.uint8).fill_(workloads.fp8_nan_code)
+        amax = {"k": 0.0, "v": 0.0}
+        for sq in range(case.num_seqs):
+            for w in amax:
+                amax[w] = max(amax[w], float(case.raw_kv(layer, sq, dev, w).abs().max().item()))
+        ks = float(np.float32(amax["k"]) / np.float32(448.0))
+        vs = float(np.float32(amax["v"]) / np.float32(448.0))
+        for sq in range(case.num_seqs):
+            pkv.append(case.raw_kv(layer, sq, dev, "k"), case.raw_kv(layer, sq, dev, "v"),
+                       case.slots(sq, 0, n).to(dev), kc, vc, ks, vs)
+        layers.append({"kc": kc, "vc": vc, "ks": ks, "vs": vs, "q": case.raw_q(layer, dev),
+                       "k_new": case.raw_new(layer, dev, "k"), "v_new": case.raw_new(layer, dev, "v")})
+    t = {"case": case, "layers": layers, "bt": case.block_tables.to(dev),
+         "cl": torch.full((case.num_seqs,), n, dtype=torch.int32, device=dev),
+         "last_slots": torch.cat([case.slots(sq, n - 1, n) for sq in range(case.num_seqs)]).to(dev)}
+    t["out"] = torch.empty_like(layers[0]["q"])
+    need = pkv.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                                      case.block_tables.shape[1], case.block_size)
+    t["ws"] = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    return t
+
+
+def run_long_context_decode(pkv, t, lay):
+    c = t["case"]
+    pkv.decode_attn(lay["q"], lay["kc"], lay["vc"], t["bt"], t["cl"], c.scale, out=t["out"],
+                    k_scale=lay["ks"], v_scale=lay["vs"], workspace=t["ws"])
+
+
+def run_long_context_step(pkv, t):
+    """One decode step of the whole model's attention: per layer, write the
+    newest token's K, V (position 99,999) and attend over all 100,000."""
+    for lay in t["layers"]:
+        pkv.append(lay["k_new"], lay["v_new"], t["last_slots"], lay["kc"], lay["vc"], lay["ks"], lay["vs"])
+        run_long_context_decode(pkv, t, lay)
 
 
 def run_decode_call(pkv, t):
@@ -228,7 +281,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+    ap.add_argument("--no-long-context", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill", "long"], default=None,
                     help="run only this kernel's launches (for profiler runs)")
     ap.add_argument("--ingest-profile", nargs=5, metavar=("NAME", "TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "KERNEL_REGEX"),
                     help="summarise rocprofv3 csv output into profiles/ (no GPU needed)")
@@ -252,8 +306,10 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     if args.only is not None:
-        t = (decode_setup if args.only == "decode" else prefill_setup)(torch, pkv, workloads, dev)
-        call = run_decode_call if args.only == "decode" else run_prefill_call
+        setup = {"decode": decode_setup, "prefill": prefill_setup, "long": long_context_setup}[args.only]
+        call = {"decode": run_decode_call, "prefill": run_prefill_call,
+                "long": lambda pkv, t: run_long_context_decode(pkv, t, t["layers"][0])}[args.only]
+        t = setup(torch, pkv, workloads, dev) if args.only != "long" else setup(torch, pkv, workloads, dev, 1)
         for _ in range(args.warmup + args.steps):
             call(pkv, t)
         torch.cuda.synchronize()
@@ -348,6 +404,50 @@ def main() -> int:
                          "avg_launch_us": round(pre_ms * 1e3, 2)},
             "suffix_tokens_per_s": round(int(pc.suffix_lens.sum()) / (pre_ms * 1e-3), 1),
         }
+
+    # ---------------- long-context fp8 decode: 32 layers per step ----------------
+    if not args.no_long_context:
+        if not args.no_prefill:
+            del p
+        torch.cuda.empty_cache()
+        lt = long_context_setup(torch, pkv, workloads, dev)
+        lc = lt["case"]
+        lsteps = max(3, args.steps // 10)
+        for _ in range(max(1, args.warmup // 5)):
+            run_long_context_step(pkv, lt)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(lsteps):
+            run_long_context_step(pkv, lt)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        lms = e0.elapsed_time(e1) / lsteps
+        lbytes = lc.kv_read_bytes_per_layer() * lc.num_layers
+        timer = EventTimer(torch, stream, lc.num_layers * lsteps)
+        for _ in range(lsteps):
+            for lay in lt["layers"]:
+                with timer:
+                    run_long_context_decode(pkv, lt, lay)
+        lay_ms = timer.mean_ms()
+        lay_gbs = lc.kv_read_bytes_per_layer() / (lay_ms * 1e-3) / 1e9
+        ltraffic = load_traffic("decode_long_context_8x100k_fp8", KERNEL_SOURCES)
+        result["long_context_fp8"] = {
+            "metric": "long-context fp8 decode KV-read GB/s", "value": round(lbytes / (lms * 1e-3) / 1e9, 1),
+            "unit": "GB/s", "ms_per_step": round(lms, 4), "steps": lsteps,
+            "tokens_per_s": round(lc.num_seqs / (lms * 1e-3), 1),
+            "config": {"workload": "8 sequences x 100,000 tokens, 32 layers, 32/8 heads, d=128, fp8 e4m3fn KV "
+                                   "(per-layer K/V scales), bf16 q/out, B=32; step = append newest token + "
+                                   "decode, every layer", "kv_bytes_per_step": lbytes},
+            "roofline": {"kernel": "pkv_decode_attn on one layer (decode_kernel + decode_combine_kernel)",
+                         "bound": "hbm", "achieved": round(lay_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(lay_gbs / HBM_PEAK_GBS, 4),
+                         "traffic": None if ltraffic is None else ltraffic["bytes_per_launch"],
+                         "avg_launch_us": round(lay_ms * 1e3, 2),
+                         "algorithmic_bytes_per_launch": lc.kv_read_bytes_per_layer()},
+        }
+        del lt
+        torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case)

@@ -1,0 +1,88 @@
+"""Long-context fp8 decode at full size: 8 sequences x 100,000 tokens, 32/8
+heads, d=128, e4m3fn KV with one fp32 scale per layer for K and one for V,
+B=32, shuffled 25,000-block pool shared by one block table per sequence.
+
+Layers 0 and 31 are built in full on the GPU (every token quantized by
+pkv_append from N(0,1) rows drawn on the device) and decoded once. The oracle
+then re-derives, on the host, the expected codes and outputs for a sample of
+(sequence, KV head) pairs: the cache bytes of those pairs must match bit for
+bit, and the outputs of their query heads within 2e-2 (+ half a bf16 ulp)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import prefix_reuse_amd as pkv
+import workloads
+from _helpers import TOL, report
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE_SEQS = (0, 7)
+SAMPLE_KV_HEADS = (0, 7)
+
+
+def _layer_on_gpu(case: workloads.LongContextFp8Case, layer: int, dev):
+    n = case.context_len
+    kc, vc = pkv.empty_caches(case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim,
+                              torch.float8_e4m3fn, dev)
+    kc.view(torch.uint8).fill_(workloads.fp8_nan_code)
+    vc.view(torch.uint8).fill_(workloads.fp8_nan_code)
+    # one scale per layer per K/V: amax over the layer's rows / 448, in fp32
+    amax = {"k": 0.0, "v": 0.0}
+    for s in range(case.num_seqs):
+        for w in amax:
+            amax[w] = max(amax[w], float(case.raw_kv(layer, s, dev, w).abs().max().item()))
+    k_scale = float(np.float32(amax["k"]) / np.float32(448.0))
+    v_scale = float(np.float32(amax["v"]) / np.float32(448.0))
+    for s in range(case.num_seqs):
+        pkv.append(case.raw_kv(layer, s, dev, "k"), case.raw_kv(layer, s, dev, "v"),
+                   case.slots(s, 0, n).to(dev), kc, vc, k_scale, v_scale)
+    q = case.raw_q(layer, dev)
+    out = pkv.decode_attn(q, kc, vc, case.block_tables.to(dev),
+                          torch.full((case.num_seqs,), n, dtype=torch.int32, device=dev), case.scale,
+                          k_scale=k_scale, v_scale=v_scale)
+    torch.cuda.synchronize()
+    return kc, vc, q, out, k_scale, v_scale
+
+
+@pytest.mark.parametrize("layer", [0, 31])
+def test_config5_long_context_fp8_sampled(layer):
+    dev = torch.device("cuda")
+    case = workloads.config5_long_context_fp8()
+    n, bsz, d = case.context_len, case.block_size, case.head_dim
+    group = case.num_q_heads // case.num_kv_heads
+    print(f"config5 layer {layer}: {case.num_seqs} x {n} tokens, fp8, B={bsz}", flush=True)
+    kc, vc, q, out, k_scale, v_scale = _layer_on_gpu(case, layer, dev)
+    assert torch.isfinite(out.float()).all()
+    q_host = q.float().cpu().double().numpy()
+    out_host = out.float().cpu().double().numpy()
+    nblk = n // bsz
+    ident = np.arange(nblk, dtype=np.int64)[None, :]
+    worst = 0.0
+    for s in SAMPLE_SEQS:
+        bt = case.block_tables[s].long().to(dev)
+        for h in SAMPLE_KV_HEADS:
+            # expected codes of this (sequence, KV head), from the raw rows
+            raw_k = case.raw_kv(layer, s, dev, "k")[:, h].cpu().numpy()
+            raw_v = case.raw_kv(layer, s, dev, "v")[:, h].cpu().numpy()
+            ek = oracle.e4m3fn_quantize(raw_k, k_scale)                   # [n, d]
+            ev = oracle.e4m3fn_quantize(raw_v, v_scale)
+            # bytes the GPU stored for this sequence's blocks, in logical order
+            gk = kc.view(torch.uint8)[bt, h].reshape(n, d).cpu().numpy()  # [nblk, B, d]
+            gv = vc.view(torch.uint8)[bt, h].permute(0, 2, 1).reshape(n, d).cpu().numpy()
+            bad_k = int((gk != ek).sum())
+            bad_v = int((gv != ev).sum())
+            print(f"  seq {s} kv head {h}: code mismatches K={bad_k} V={bad_v}", flush=True)
+            assert bad_k == 0 and bad_v == 0
+            # oracle decode over this sequence's blocks laid out in logical order
+            # (outputs do not depend on the physical placement of blocks)
+            heads = list(range(h * group, (h + 1) * group))
+            ref = oracle.decode_attention(
+                q_host[s:s + 1, heads], ek.reshape(nblk, bsz, 1, d), ev.reshape(nblk, bsz, 1, d),
+                ident, np.array([n]), case.scale, fp8=True, k_scale=k_scale, v_scale=v_scale)
+            got = out_host[s:s + 1, heads]
+            worst = max(worst, report(f"config5 L{layer} s{s} h{h}", got, ref, torch.bfloat16, TOL["fp8"]))
+    assert worst <= 1.0
