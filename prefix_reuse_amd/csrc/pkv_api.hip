@@ -326,8 +326,9 @@ int pkv_suffix_prefill_attn(const pkv_tensor* q, const pkv_tensor* k_cache, cons
   p.out = out->data; p.o_s0 = out->stride[0]; p.o_s1 = out->stride[1];
   p.num_reqs = (int32_t)R; p.hq = (int32_t)hq; p.hkv = cg.hkv; p.group = (int32_t)(hq / cg.hkv);
   p.num_blocks = (int32_t)cg.num_blocks; p.total_rows = total;
-  // upper bound on row tiles per KV head: sum_r ceil(S_r * G / 128) <= ceil(total * G / 128) + R
-  const int64_t tiles = (total * p.group + 127) / 128 + R;
+  // upper bound on row tiles per KV head: sum_r ceil(S_r * G / W) <= ceil(total * G / W) + R
+  constexpr int64_t W = pkv::kPrefillRowsPerWg;
+  const int64_t tiles = (total * p.group + W - 1) / W + R;
   if (tiles * cg.hkv > INT32_MAX) return fail(PKV_ERR_SHAPE, "problem too large for one launch");
   p.tiles_per_head = (int32_t)tiles;
   p.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * pkv::kLog2eHost;

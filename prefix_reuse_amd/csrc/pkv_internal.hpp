@@ -38,6 +38,10 @@ struct DecodeParams {
   float v_scale;
 };
 
+// Suffix-prefill work-group: kPrefillWaves waves of 32 (token, head) rows each.
+constexpr int kPrefillWaves = 8;
+constexpr int kPrefillRowsPerWg = 32 * kPrefillWaves;
+
 struct PrefillParams {
   const void* q; int64_t q_s0, q_s1;  // [total, Hq, D]
   const void* k_cache; const void* v_cache;

@@ -10,27 +10,30 @@
 // Design (a dense contraction, so it runs on the matrix cores):
 //  * Rows of the problem are (suffix token, query head of the GQA group)
 //    pairs, token-major, so one K/V read serves all G heads of a KV head and a
-//    tile's causal diagonal spans few tokens. A work-group of 4 waves owns 128
-//    rows of one (request, KV head); each wave owns 32 rows, whose Q^T stays in
-//    registers.
-//  * Keys are consumed 64 per stage, double buffered in LDS (the next stage's
-//    loads are in flight while this one is computed; one barrier per stage).
-//    16-bit K and V go from global memory straight to LDS (global_load_lds);
-//    fp8 tiles are staged through registers and converted. Values of keys past
-//    the end are zeroed in LDS (they meet P = 0, and 0 * NaN would be NaN).
-//    Both LDS tiles are XOR-swizzled so that the matrix-core operand reads are
-//    free of bank conflicts. Block ids come from scalar loads two stages ahead.
+//    tile's causal diagonal spans few tokens. A work-group of 8 waves (one
+//    per CU, two per SIMD) owns 256 rows of one (request, KV head); each wave
+//    owns 32 rows, whose Q^T stays in registers.
+//  * Keys are consumed 64 per stage through a ring of four LDS buffers per
+//    operand. 16-bit K and V tiles go from global memory straight to LDS
+//    (global_load_lds, one 1 KB load per wave lying inside a single cache
+//    block, addressed by a scalar block base plus a fixed lane offset), three
+//    stages ahead of use; fp8 tiles are staged through registers and
+//    converted exactly. V^T tiles keep the cache's own [d][B] block layout in
+//    LDS. Both LDS layouts are XOR-swizzled so that the matrix-core operand
+//    reads are free of bank conflicts. Block ids come from scalar loads.
 //  * Per wave and 32-key sub-tile, on v_mfma_f32_32x32x16:
 //      S^T[key][row] = K[key][:] . Q[row][:]
 //      O^T[dim][row] += V^T[dim][keys] . P^T[keys][row]
 //    K rows are read in a permuted order so that each lane ends up holding 16
-//    consecutive keys of one row: the B operand of the PV product.
+//    consecutive keys of one row: the B operand of the PV product. The score
+//    product runs two sub-tiles ahead of the value product; each step reads
+//    its operands from LDS first, computes a softmax while they arrive, then
+//    issues its 24 (16) products back to back.
 //  * Precision of P in the PV product: with f16 operands P is rounded to f16
 //    (11 bits, P is in [0, 2^8] thanks to the lazy rescale below). With bf16
 //    operands P would carry only 8 bits - too few for 2e-3 on short contexts -
 //    so P goes in as bf16(P) + bf16(P - bf16(P)): two products on the matrix
-//    cores, which have room to spare, instead of converting V on the vector
-//    units, which do not. fp8 V is converted exactly to f16 while staging.
+//    cores. fp8 V is converted exactly to f16 while staging.
 //  * Online softmax in base 2 with the scale folded into one FMA per score and
 //    the raw v_exp_f32 (results below 2^-126 flush to 0); the running max moves
 //    only when a row's max grows by more than 2^8 (lazy rescale), so the
@@ -45,17 +48,19 @@
 namespace pkv {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = kPrefillWaves;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsWave = 32;
 constexpr int kRowsWg = kRowsWave * kWaves;
-constexpr int kStage = 64;     // keys per LDS stage
+constexpr int kStage = 64;     // keys per LDS stage = two 32-key sub-tiles
+constexpr int kRing = 4;       // LDS buffers per operand (stage s lives in buffer s % kRing)
 constexpr float kLazy = 8.0f;  // log2 headroom before the running max moves
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(4))) const int32_t sconst_i32;  // read with scalar loads
 
-// ---- LDS tile layouts (element offsets), with XOR swizzles of 16-byte pieces ----
-// K: [kStage keys][D] in the operand type; piece = 8 dims.
+// ---- LDS tile layouts (element offsets), XOR swizzles of 16-byte pieces ----
+// K: [kStage keys][D] in the Q type; piece = 8 dims.
 template <int D>
 __device__ __forceinline__ int k_swz(int row) {
   if constexpr (D == 128) return (row & 7) | (((row >> 4) & 1) << 3);
@@ -65,166 +70,202 @@ template <int D>
 __device__ __forceinline__ int k_off(int row, int piece) {  // piece in [0, D/8)
   return row * D + ((piece ^ k_swz<D>(row)) << 3);
 }
-// V^T: [D][kStage keys] in f16; piece = 8 keys.
-__device__ __forceinline__ int v_off(int d, int piece) {  // piece in [0, 8)
-  return d * kStage + ((piece ^ ((d >> 1) & 7)) << 3);
+// V^T: one [D][BLK] tile per cache block of the stage, block-major, exactly as
+// the cache stores it; piece = 8 keys, swizzled within the tile's rows.
+template <int D, int BLK>
+__device__ __forceinline__ int v_off(int blk, int d, int piece) {  // piece in [0, BLK/8)
+  constexpr int kPpr = BLK / 8;
+  constexpr int kSh = kPpr == 2 ? 3 : 2;
+  return (blk * D + d) * BLK + ((piece ^ ((d >> kSh) & (kPpr - 1))) << 3);
+}
+
+__device__ __forceinline__ int sel4(int b0, int b1, int b2, int b3, int i) {  // i uniform
+  return i < 2 ? (i == 0 ? b0 : b1) : (i == 2 ? b2 : b3);
+}
+
+// A wave-uniform address kept in scalar registers, so that a load can add a
+// 32-bit per-lane offset to it without vector 64-bit arithmetic.
+__device__ __forceinline__ const char* uniform_ptr(const void* base, int64_t off) {
+  const uint64_t b = (uint64_t)base + (uint64_t)off;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
+// One wave-wide direct-to-LDS load of 16 bytes per lane: lane l reads
+// base + voff and writes LDS bytes lds + 16l .. +15 (base and lds uniform).
+// Issued as inline assembly so that the compiler does not see it: its own
+// wait insertion would otherwise drain every direct load in flight before each
+// LDS read, because it cannot tell which buffer a load writes. The kernel
+// orders these loads itself with explicit waits before its barriers.
+__device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(lds), "v"(voff), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_address(const char* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p);
 }
 
 template <typename TQ, typename TC>
 struct Types {
   static constexpr bool kFp8 = std::is_same<TC, uint8_t>::value;
-  static constexpr bool kDirect = !kFp8;  // 16-bit tiles land in LDS as stored
   // PV operand type: the cache's own 16-bit type, f16 for an fp8 cache
   typedef typename std::conditional<kFp8, f16_t, TC>::type VOp;
   static constexpr bool kSplitP = std::is_same<VOp, bf16_t>::value;
 };
 
-template <typename TQ, typename TC, int D, int BLK>
-struct Stage {
-  typedef Types<TQ, TC> T;
-  typedef typename T::VOp VOp;
-  static constexpr int kBlocks = kStage / BLK;  // blocks per stage
-  // fp8 register staging: K pieces of 16 dims (16 codes), V pieces of 8 keys
-  // (8 codes); an empty struct for 16-bit tiles, which go straight to LDS
-  static constexpr int kKPieces = kStage * (D / 16) / kThreads;
-  static constexpr int kVPieces = D * (kStage / 8) / kThreads;
-  struct Fp8Regs {
-    u32x4 kr[kKPieces];
-    u32x2 vr[kVPieces];
+// Physical block ids of the kStage/BLK blocks of one stage (plain ints:
+// arrays here end up in scratch). Scalar loads; entries past the last live
+// block repeat it.
+struct Ids {
+  int b0, b1, b2, b3;
+};
+template <int BLK>
+__device__ __forceinline__ Ids load_ids(const int32_t* bt, int st, int last, int num_blocks) {
+  constexpr int kB = kStage / BLK;
+  const sconst_i32* t = (const sconst_i32*)bt;
+  auto id = [&](int i) {
+    const int v = t[min(st * kB + i, last)];
+    return min(max(v, 0), num_blocks - 1);
   };
-  struct NoRegs {};
-  typedef typename std::conditional<T::kDirect, NoRegs, Fp8Regs>::type Regs;
+  Ids r;
+  r.b0 = id(0);
+  r.b1 = id(1);
+  r.b2 = kB == 4 ? id(2) : 0;
+  r.b3 = kB == 4 ? id(3) : 0;
+  return r;
+}
 
-  // Block ids of one stage, kept in four plain ints (arrays or structs here
-  // end up in LDS or scratch). Loaded with scalar loads: pointer and index
-  // are uniform; entries past the end repeat the last block with a live key.
-  __device__ __forceinline__ static void load_ids(int& b0, int& b1, int& b2, int& b3, const int32_t* bt, int st,
-                                                  int kv_len, int max_blocks, int num_blocks) {
-    static_assert(kBlocks == 2 || kBlocks == 4, "16- or 32-token blocks");
-    const int last = min((kv_len - 1) / BLK, max_blocks - 1);
-    auto id = [&](int i) {
-      const int jb = min(st * kBlocks + i, last);
-      return min(max(bt[jb], 0), num_blocks - 1);
-    };
-    b0 = id(0);
-    b1 = id(1);
-    b2 = kBlocks == 4 ? id(2) : 0;
-    b3 = kBlocks == 4 ? id(3) : 0;
-  }
-  __device__ __forceinline__ static int pick(int b0, int b1, int b2, int b3, int i) {  // i in [0, kBlocks)
-    if constexpr (kBlocks == 2) return i == 0 ? b0 : b1;
-    else return i < 2 ? (i == 0 ? b0 : b1) : (i == 2 ? b2 : b3);
-  }
+// 16-bit caches: every load is one wave-wide global_load_lds of 1 KB that
+// lies inside a single cache block, so its address is a scalar block base
+// plus a per-lane offset fixed for the whole kernel, and its LDS destination
+// is a contiguous 1 KB (lane l writes bytes 16l .. 16l+15).
+template <int D, int BLK>
+struct Dma {
+  static constexpr int kKeysPerInst = 1024 / (D * 2);            // K rows per load
+  static constexpr int kKInst = kStage / kKeysPerInst / kWaves;    // K loads per wave per stage
+  static constexpr int kChunks = D * BLK * 2 / 1024;             // 1 KB pieces of a V tile
+  static constexpr int kVInst = D * kStage * 2 / 1024 / kWaves;    // V loads per wave per stage
+  static constexpr int kPpr = BLK / 8;
+  static constexpr int kSh = kPpr == 2 ? 3 : 2;
+  static constexpr int kRowsPerChunk = 1024 / (BLK * 2);
+  uint32_t koff[kKInst], voff[kVInst];
 
-  // Issue this thread's loads of stage `st` (keys st*kStage ..) with the
-  // stage's block ids: direct-to-LDS for 16-bit tiles, registers for fp8.
-  __device__ __forceinline__ static void issue(Regs& rg, const TC* kbase, const TC* vbase, int b0, int b1, int b2,
-                                               int b3, int hk, int hkv, int st, int kv_len, TQ* k_lds, VOp* v_lds,
-                                               int wave, int lane) {
-    const int key0 = st * kStage;
-    const int64_t tile = (int64_t)BLK * D;
-    if constexpr (T::kDirect) {
-      // K: 1 KB per instruction, lane-linear, rows of D*2 bytes
-      constexpr int kInst = kStage * D * 2 / 1024;
-      constexpr int kRowsPerInst = 1024 / (D * 2);
-      constexpr int kLanesPerRow = 64 / kRowsPerInst;
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-      for (int i = 0; i < kInst / kWaves; ++i) {
-        const int j = wave * (kInst / kWaves) + i;
-        int row = j * kRowsPerInst + lane / kLanesPerRow;
-        const int piece = (lane % kLanesPerRow) ^ k_swz<D>(row);
-        if (key0 + row >= kv_len) row = kv_len - 1 - key0 >= 0 ? kv_len - 1 - key0 : 0;  // any live row
-        const TC* src = kbase + ((int64_t)pick(b0, b1, b2, b3, row / BLK) * hkv + hk) * tile + (int64_t)(row % BLK) * D + piece * 8;
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (lds_void*)(k_lds + j * 512), 16, 0, 0);
-      }
-      // V^T: 1 KB per instruction = 8 rows of 64 keys
-      constexpr int kVInst = D * kStage * 2 / 1024;
+    for (int i = 0; i < kKInst; ++i) {
+      const int r = (i * kWaves + wave) * kKeysPerInst + lane / (D / 8);
+      const int piece = (lane % (D / 8)) ^ k_swz<D>(r);
+      koff[i] = (uint32_t)(((r % BLK) * D + piece * 8) * 2);
+    }
 #pragma unroll
-      for (int i = 0; i < kVInst / kWaves; ++i) {
-        const int j = wave * (kVInst / kWaves) + i;
-        const int d = j * 8 + lane / 8;
-        const int piece = (lane % 8) ^ ((d >> 1) & 7);
-        const int k8 = piece * 8;  // first key of the piece within the stage
-        const TC* src = vbase + ((int64_t)pick(b0, b1, b2, b3, k8 / BLK) * hkv + hk) * tile + (int64_t)d * BLK + (k8 % BLK);
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (lds_void*)(v_lds + j * 512), 16, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kKPieces; ++i) {  // 16 codes = dims 16q .. 16q+15 of one key
-        const int pi = lane + 64 * (wave + kWaves * i);
-        const int row = pi / (D / 16), q = pi % (D / 16);
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (key0 + row < kv_len)
-          w = load_u32x4(kbase + ((int64_t)pick(b0, b1, b2, b3, row / BLK) * hkv + hk) * tile + (int64_t)(row % BLK) * D + q * 16);
-        rg.kr[i] = w;
-      }
-#pragma unroll
-      for (int i = 0; i < kVPieces; ++i) {  // 8 codes = keys 8p .. 8p+7 of one dim
-        const int pi = lane + 64 * (wave + kWaves * i);
-        const int d = pi / (kStage / 8), piece = pi % (kStage / 8);
-        u32x2 w = {0u, 0u};
-        if (key0 + piece * 8 < kv_len)
-          w = load_u32x2(vbase + ((int64_t)pick(b0, b1, b2, b3, piece * 8 / BLK) * hkv + hk) * tile + (int64_t)d * BLK + (piece * 8) % BLK);
-        rg.vr[i] = w;
-      }
+    for (int i = 0; i < kVInst; ++i) {
+      const int c = i * kWaves + wave;
+      const int d = (c % kChunks) * kRowsPerChunk + lane / kPpr;
+      const int piece = (lane % kPpr) ^ ((d >> kSh) & (kPpr - 1));
+      voff[i] = (uint32_t)((d * BLK + piece * 8) * 2);
     }
   }
-
-  // fp8: convert the register-staged pieces of stage `st` and write them to LDS.
-  __device__ __forceinline__ static void commit(Regs& rg, int st, int kv_len, TQ* k_lds, VOp* v_lds, int wave,
-                                                int lane) {
-    if constexpr (!T::kDirect) {
-      typedef typename Frag<TQ>::type F;
+  __device__ __forceinline__ void issue_k(const void* cache, int64_t bstride, int64_t hoff, Ids ids, char* dst,
+                                          int wave) const {
 #pragma unroll
-      for (int i = 0; i < kKPieces; ++i) {
-        const int pi = lane + 64 * (wave + kWaves * i);
-        const int row = pi / (D / 16), q = pi % (D / 16);
-        u32x2 lo = {rg.kr[i][0], rg.kr[i][1]}, hi = {rg.kr[i][2], rg.kr[i][3]};
-        *reinterpret_cast<F*>(k_lds + k_off<D>(row, 2 * q)) = fp8x8_to<TQ>(lo);
-        *reinterpret_cast<F*>(k_lds + k_off<D>(row, 2 * q + 1)) = fp8x8_to<TQ>(hi);
-      }
-      const int key0 = st * kStage;
-#pragma unroll
-      for (int i = 0; i < kVPieces; ++i) {
-        const int pi = lane + 64 * (wave + kWaves * i);
-        const int d = pi / (kStage / 8), piece = pi % (kStage / 8);
-        f16x8 f = fp8x8_to<f16_t>(rg.vr[i]);  // exact: every e4m3fn value is an f16 value
-        const int pos = key0 + piece * 8;
-        if (pos + 8 > kv_len) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = pos + e < kv_len ? f[e] : (f16_t)0.f;
-        }
-        *reinterpret_cast<f16x8*>(v_lds + v_off(d, piece)) = f;
-      }
+    for (int i = 0; i < kKInst; ++i) {
+      const int r0 = (i * kWaves + wave) * kKeysPerInst;
+      const int bid = sel4(ids.b0, ids.b1, ids.b2, ids.b3, r0 / BLK);
+      const char* base = uniform_ptr(cache, (int64_t)bid * bstride + hoff);
+      dma16(base, koff[i], lds_address(dst + r0 * D * 2));
     }
   }
-
-  // 16-bit tiles: after the stage has landed, zero V of keys >= kv_len (the
-  // direct loads brought whatever those cache slots hold). Call with all
-  // threads of the work-group; only the stage holding kv_len has such keys.
-  __device__ __forceinline__ static void zero_tail(int st, int kv_len, VOp* v_lds, int tid) {
-    const int key0 = st * kStage;
-    const int first = kv_len - key0;  // first dead key within the stage
-    const int dead = kStage - first;
-    for (int idx = tid; idx < D * dead; idx += kThreads) {
-      const int d = idx / dead, k = first + idx % dead;
-      v_lds[v_off(d, k / 8) + (k % 8)] = (VOp)0.f;
+  __device__ __forceinline__ void issue_v(const void* cache, int64_t bstride, int64_t hoff, Ids ids, char* dst,
+                                          int wave) const {
+#pragma unroll
+    for (int i = 0; i < kVInst; ++i) {
+      const int c = i * kWaves + wave;
+      const int bid = sel4(ids.b0, ids.b1, ids.b2, ids.b3, c / kChunks);
+      const char* base = uniform_ptr(cache, (int64_t)bid * bstride + hoff);
+      dma16(base, voff[i], lds_address(dst + c * 1024));
     }
   }
 };
 
+// fp8 caches: 16-code pieces staged through registers and converted exactly
+// (K to the Q type, V to f16) when written to LDS.
+template <typename TQ, int D, int BLK>
+struct Fp8Stage {
+  static constexpr int kPieces = kStage * D / 16;               // per stage, K and V alike
+  static constexpr int kP = (kPieces + kThreads - 1) / kThreads;  // pieces per thread
+  static constexpr int kPiecesPerTile = D * BLK / 16;
+  u32x4 kr[kP], vr[kP];
+
+  __device__ __forceinline__ void issue_k(const uint8_t* cache, int64_t bstride, int64_t hoff, Ids ids,
+                                          int tid) {
+#pragma unroll
+    for (int i = 0; i < kP; ++i) {
+      const int pi = tid + kThreads * i;
+      if (kPieces % kThreads != 0 && pi >= kPieces) break;
+      const int row = pi / (D / 16), q = pi % (D / 16);
+      const int bid = sel4(ids.b0, ids.b1, ids.b2, ids.b3, __builtin_amdgcn_readfirstlane(row / BLK));
+      kr[i] = load_u32x4(cache + (int64_t)bid * bstride + hoff + (row % BLK) * D + q * 16);
+    }
+  }
+  __device__ __forceinline__ void issue_v(const uint8_t* cache, int64_t bstride, int64_t hoff, Ids ids,
+                                          int tid) {
+#pragma unroll
+    for (int i = 0; i < kP; ++i) {
+      const int pi = tid + kThreads * i;
+      if (kPieces % kThreads != 0 && pi >= kPieces) break;
+      const int tile = pi / kPiecesPerTile, rem = pi % kPiecesPerTile;
+      const int d = rem / (BLK / 16), h = rem % (BLK / 16);
+      const int bid = sel4(ids.b0, ids.b1, ids.b2, ids.b3, __builtin_amdgcn_readfirstlane(tile));
+      vr[i] = load_u32x4(cache + (int64_t)bid * bstride + hoff + d * BLK + h * 16);
+    }
+  }
+  __device__ __forceinline__ void commit_k(TQ* k_lds, int tid) const {
+    typedef typename Frag<TQ>::type F;
+#pragma unroll
+    for (int i = 0; i < kP; ++i) {
+      const int pi = tid + kThreads * i;
+      if (kPieces % kThreads != 0 && pi >= kPieces) break;
+      const int row = pi / (D / 16), q = pi % (D / 16);
+      const u32x2 lo = {kr[i][0], kr[i][1]}, hi = {kr[i][2], kr[i][3]};
+      *reinterpret_cast<F*>(k_lds + k_off<D>(row, 2 * q)) = fp8x8_to<TQ>(lo);
+      *reinterpret_cast<F*>(k_lds + k_off<D>(row, 2 * q + 1)) = fp8x8_to<TQ>(hi);
+    }
+  }
+  __device__ __forceinline__ void commit_v(f16_t* v_lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kP; ++i) {
+      const int pi = tid + kThreads * i;
+      if (kPieces % kThreads != 0 && pi >= kPieces) break;
+      const int tile = pi / kPiecesPerTile, rem = pi % kPiecesPerTile;
+      const int d = rem / (BLK / 16), h = rem % (BLK / 16);
+      const u32x2 lo = {vr[i][0], vr[i][1]}, hi = {vr[i][2], vr[i][3]};
+      // exact: every e4m3fn value is an f16 value
+      *reinterpret_cast<f16x8*>(v_lds + v_off<D, BLK>(tile, d, 2 * h)) = fp8x8_to<f16_t>(lo);
+      *reinterpret_cast<f16x8*>(v_lds + v_off<D, BLK>(tile, d, 2 * h + 1)) = fp8x8_to<f16_t>(hi);
+    }
+  }
+};
+
+// P^T fragments of one 32-key sub-tile: the B operands of the two PV steps,
+// as rounded values and (bf16 only) the rounding remainders.
+template <typename FV>
+struct PFrag {
+  FV hi[2], lo[2];
+};
+
 template <typename TQ, typename TC, int D, int BLK>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   typedef Types<TQ, TC> T;
   typedef typename T::VOp VOp;
   typedef typename Frag<TQ>::type F;
   typedef typename Frag<VOp>::type FV;
-  typedef Stage<TQ, TC, D, BLK> STG;
   constexpr int QS = D / 16;  // k-steps of the score product
   constexpr int NT = D / 32;  // dim tiles of the output
-  constexpr int kKElems = kStage * D, kVElems = D * kStage;
-  __shared__ __attribute__((aligned(16))) TQ k_lds_all[2 * kKElems];
-  __shared__ __attribute__((aligned(16))) VOp v_lds_all[2 * kVElems];
+  constexpr int kKBytes = kStage * D * (int)sizeof(TQ);
+  constexpr int kVBytes = kStage * D * (int)sizeof(VOp);
+  __shared__ __attribute__((aligned(1024))) char lds[kRing * (kKBytes + kVBytes)];
+  char* const k_lds0 = lds;                    // K stages: buffers 0 .. kRing-1
+  char* const v_lds0 = lds + kRing * kKBytes;  // V stages: buffers 0 .. kRing-1
 
   // ---- which (KV head, request, row tile) ----
   const int logical = xcd_remap(blockIdx.x, p.hkv * p.tiles_per_head);
@@ -255,16 +296,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   const int lane = tid % 64;
   const int h0 = lane / 32, c32 = lane % 32;
 
-  const int q0 = tile * kRowsWg;                  // first row of the work-group
+  const int q0 = tile * kRowsWg;  // first row of the work-group
   const int tok_last_wg = min(S - 1, (q0 + kRowsWg - 1) / p.group);
-  const int wq0 = q0 + wave * kRowsWave;          // first row of this wave
+  const int wq0 = q0 + wave * kRowsWave;  // first row of this wave
   const int tok_first_w = wq0 / p.group;
   const int tok_last_w = min(S - 1, (wq0 + kRowsWave - 1) / p.group);
   const bool wave_active = wq0 < rows_r;
   const int keys_wg = min(kv_len, P + tok_last_wg + 1);
   const int nst = (keys_wg + kStage - 1) / kStage;
   const int keys_w = wave_active ? min(kv_len, P + tok_last_w + 1) : 0;
+  const int nsub = (keys_w + 31) / 32;                        // 32-key sub-tiles of this wave
   const int full_keys_w = min(P + tok_first_w + 1, kv_len);  // keys below need no mask in this wave
+  if (nst == 0) return;                                      // uniform over the work-group
 
   // ---- Q^T fragments for this lane's row ----
   const int row = wq0 + c32;
@@ -280,127 +323,306 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     qf[c] = v;
   }
   const int lim = P + tok;  // last key position this row may see
-  // permuted key row (within a 32-key sub-tile) read by this lane for the score A operand
-  const int krow_perm = 16 * ((c32 % 8) / 4) + 4 * (c32 / 8) + (c32 % 4);
+  const float c2 = p.qk_scale_log2;
 
+  // LDS byte addresses of this lane's operands (buffer 0, sub-tile 0)
+  // score A operand: permuted key row so that each lane ends up with 16
+  // consecutive keys of one row - the B operand of the PV product
+  const int krow = 16 * ((c32 % 8) / 4) + 4 * (c32 / 8) + (c32 % 4);
+  // k-step c reads piece (2c + h0) ^ swz of row krow, i.e. byte address
+  // kx ^ 32c: the swizzle's upper bits permute whole 32-byte piece pairs
+  const int kx = k_off<D>(krow, h0) * (int)sizeof(TQ);
+  static_assert(sizeof(TQ) == 2, "16-bit score operands");
+  // PV A operand, step u of a sub-tile: dim 32n + c32, keys 16*h0 + 8u .. +8
+  int vaddr[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if constexpr (BLK == 16) vaddr[u] = v_off<D, BLK>(h0, c32, u) * (int)sizeof(VOp);  // block 2t + h0
+    else vaddr[u] = v_off<D, BLK>(0, c32, 2 * h0 + u) * (int)sizeof(VOp);               // block t
+  }
+  // byte distance between sub-tiles t = 0 and 1 of a stage, and between dim tiles
+  constexpr int kKSub = 32 * D * (int)sizeof(TQ);
+  constexpr int kVSub = (BLK == 16 ? 2 : 1) * D * BLK * (int)sizeof(VOp);
+  constexpr int kVDim = 32 * BLK * (int)sizeof(VOp);
+
+  // ---- loaders ----
+  const int64_t tile_bytes = (int64_t)BLK * D * (int64_t)sizeof(TC);
+  const int64_t bstride = (int64_t)p.hkv * tile_bytes;
+  const int64_t hoff = (int64_t)hk * tile_bytes;
+  const int last_blk = min((kv_len - 1) / BLK, p.max_blocks - 1);
+  typedef typename std::conditional<T::kFp8, Fp8Stage<TQ, D, BLK>, Dma<D, BLK>>::type Loader;
+  Loader ld;
+  if constexpr (!T::kFp8) ld.init(wave, lane);
+  auto issue_k = [&](int st, Ids ids) {
+    char* dst = k_lds0 + (st % kRing) * kKBytes;
+    if constexpr (T::kFp8) {
+      ld.issue_k(reinterpret_cast<const uint8_t*>(p.k_cache), bstride, hoff, ids, tid);
+      (void)dst;
+    } else {
+      ld.issue_k(p.k_cache, bstride, hoff, ids, dst, wave);
+    }
+  };
+  auto issue_v = [&](int st, Ids ids) {
+    char* dst = v_lds0 + (st % kRing) * kVBytes;
+    if constexpr (T::kFp8) {
+      ld.issue_v(reinterpret_cast<const uint8_t*>(p.v_cache), bstride, hoff, ids, tid);
+      (void)dst;
+    } else {
+      ld.issue_v(p.v_cache, bstride, hoff, ids, dst, wave);
+    }
+  };
+  // fp8: write the staged pieces of K stage `sk` and V stage `sv` (-1: none)
+  auto commit = [&](int sk, int sv) {
+    if constexpr (T::kFp8) {
+      if (sk >= 0) ld.commit_k(reinterpret_cast<TQ*>(k_lds0 + (sk % kRing) * kKBytes), tid);
+      if (sv >= 0) ld.commit_v(reinterpret_cast<f16_t*>(v_lds0 + (sv % kRing) * kVBytes), tid);
+    }
+  };
+
+  // ---- per-row softmax state and accumulators ----
   f32x16 acc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -1e30f, l_run = 0.f;  // finite start: -inf - (-inf) would be NaN
 
-  const TC* kbase = reinterpret_cast<const TC*>(p.k_cache);
-  const TC* vbase = reinterpret_cast<const TC*>(p.v_cache);
-  typename STG::Regs regs;
-  const bool tail_stage_exists = nst > 0 && kv_len < nst * kStage;
-
-  int a0 = 0, a1 = 0, a2 = 0, a3 = 0;  // block ids of stage st+1
-  int n0 = 0, n1 = 0, n2 = 0, n3 = 0;  // block ids of stage st+2
-  if (nst > 0) {
-    int z0, z1, z2, z3;
-    STG::load_ids(z0, z1, z2, z3, bt, 0, kv_len, p.max_blocks, p.num_blocks);
-    STG::issue(regs, kbase, vbase, z0, z1, z2, z3, hk, p.hkv, 0, kv_len, k_lds_all, v_lds_all, wave, lane);
-    STG::commit(regs, 0, kv_len, k_lds_all, v_lds_all, wave, lane);
-    STG::load_ids(a0, a1, a2, a3, bt, 1, kv_len, p.max_blocks, p.num_blocks);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // direct-to-LDS loads of stage 0 have landed
-  __syncthreads();
-  if constexpr (T::kDirect) {
-    if (tail_stage_exists && nst == 1) {
-      STG::zero_tail(0, kv_len, v_lds_all, tid);
-      __syncthreads();
+  // ---- per-step pieces ----
+  // operands of one step, read from LDS before the softmax so that their
+  // latency is hidden behind it
+  struct VOps {
+    FV v[2][NT];
+  };
+  struct KOps {
+    F k[QS];
+  };
+  // K^T operands of sub-tile t of the stage in K buffer `buf`; k-step c reads
+  // piece (2c + h0) ^ swz of the lane's key row, i.e. byte address kx ^ 32c
+  auto load_k = [&](int buf, int t, KOps& ko) {
+    const char* kl = k_lds0 + buf * kKBytes + t * kKSub;
+#pragma unroll
+    for (int c = 0; c < QS; ++c) ko.k[c] = *reinterpret_cast<const F*>(kl + (kx ^ (c << 5)));
+  };
+  // V^T operands of sub-tile t of the stage in V buffer `buf`
+  auto load_v = [&](int buf, int t, VOps& vo) {
+    const char* vl = v_lds0 + buf * kVBytes + t * kVSub;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) vo.v[u][n] = *reinterpret_cast<const FV*>(vl + vaddr[u] + n * kVDim);
+  };
+  // values of keys >= kv_len are zeroed: the loads brought whatever those
+  // cache slots hold, and 0 * NaN would be NaN
+  auto zero_tail = [&](VOps& vo, int key0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int kb = key0 + 16 * h0 + 8 * u;
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vo.v[u][n][e] = kb + e < kv_len ? vo.v[u][n][e] : (VOp)0.f;
     }
-  }
-
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    TQ* k_lds = k_lds_all + buf * kKElems;
-    VOp* v_lds = v_lds_all + buf * kVElems;
-    TQ* k_nxt = k_lds_all + (buf ^ 1) * kKElems;
-    VOp* v_nxt = v_lds_all + (buf ^ 1) * kVElems;
-    if (st + 1 < nst) {
-      STG::issue(regs, kbase, vbase, a0, a1, a2, a3, hk, p.hkv, st + 1, kv_len, k_nxt, v_nxt, wave, lane);
-      STG::load_ids(n0, n1, n2, n3, bt, st + 2, kv_len, p.max_blocks, p.num_blocks);
+  };
+  auto qk = [&](const KOps& ko) -> f32x16 {  // S^T[key][row], unscaled
+    f32x16 sc = {};
+#pragma unroll
+    for (int c = 0; c < QS; ++c) sc = mfma32x32x16(ko.k[c], qf[c], sc);
+    return sc;
+  };
+  auto pv = [&](const VOps& vo, const PFrag<FV>& pf) {  // O^T += V^T P^T
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n] = mfma32x32x16(vo.v[u][n], pf.hi[u], acc[n]);
+      if constexpr (T::kSplitP) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[n] = mfma32x32x16(vo.v[u][n], pf.lo[u], acc[n]);
+      }
     }
-
+  };
+  // scores of a sub-tile (in place) -> P fragments. The running max moves
+  // only when some row's max grows by more than 2^kLazy (rare); the factor
+  // the accumulators then need is returned in `alpha` and applied by the
+  // caller once the products of the previous sub-tile have been added.
+  auto softmax = [&](f32x16& sc, int key0, bool mask, PFrag<FV>& out, float& alpha) -> bool {
+    if (mask) {
+      const int kb = key0 + 16 * h0;
 #pragma unroll
-    for (int t = 0; t < kStage / 32; ++t) {
-      const int key0 = st * kStage + 32 * t;  // first key of the sub-tile
-      if (key0 < keys_w) {                    // uniform per wave
-        // scores: element i = key key0 + 16*h0 + i, row c32 (unscaled)
-        f32x16 s = {};
-        const int krow = 32 * t + krow_perm;
+      for (int i = 0; i < 16; ++i) sc[i] = (kb + i <= lim && kb + i < kv_len) ? sc[i] : -INFINITY;
+    }
+    float mx = sc[0];
 #pragma unroll
-        for (int c = 0; c < QS; ++c) {
-          const F kf = *reinterpret_cast<const F*>(k_lds + k_off<D>(krow, 2 * c + h0));
-          s = mfma32x32x16(kf, qf[c], s);
-        }
-        if (key0 + 32 > full_keys_w) {
-          const int kb = key0 + 16 * h0;
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+    {  // the other 16 keys of this row sit in lane l ^ 32
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c2;  // scale > 0: max commutes
+    }
+    const bool grow = mx > m_run + kLazy;
+    const bool any = __any(grow);
+    alpha = 1.f;
+    if (any) {
+      const float m_new = grow ? mx : m_run;
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 for rows that keep their max
+      m_run = m_new;
+      l_run *= alpha;
+    }
+    float sum = 0.f;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) s[i] = (kb + i <= lim && kb + i < kv_len) ? s[i] : -INFINITY;
-        }
-        float cmax = s[0];
+    for (int i = 0; i < 16; ++i) {
+      sc[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], c2, -m_run));
+      sum += sc[i];
+    }
+    l_run += sum;
 #pragma unroll
-        for (int i = 1; i < 16; ++i) cmax = fmaxf(cmax, s[i]);
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 32)) * p.qk_scale_log2;  // scale > 0: max commutes
-        // lazy rescale: move the running max only when it grows by more than 2^kLazy
-        const bool grow = cmax > m_run + kLazy;
-        if (__any(grow)) {
-          const float m_new = grow ? cmax : m_run;
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 for rows that keep their max
-          m_run = m_new;
-          l_run *= alpha;
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-          for (int n = 0; n < NT; ++n) acc[n] *= alpha;
-        }
-        float pr[16];
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          pr[i] = __builtin_amdgcn_exp2f(fmaf(s[i], p.qk_scale_log2, -m_run));
-          psum += pr[i];
-        }
-        l_run += psum;
-        const FV p0 = pack8<VOp>(pr), p1 = pack8<VOp>(pr + 8);
-        FV p0lo, p1lo;
+      for (int e = 0; e < 8; e += 2) {
+        const float a = sc[8 * h + e], b = sc[8 * h + e + 1];
+        const VOp ha = (VOp)a, hb = (VOp)b;
+        out.hi[h][e] = ha;
+        out.hi[h][e + 1] = hb;
         if constexpr (T::kSplitP) {
-          float lo[16];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) { lo[i] = pr[i] - (float)p0[i]; lo[8 + i] = pr[8 + i] - (float)p1[i]; }
-          p0lo = pack8<VOp>(lo);
-          p1lo = pack8<VOp>(lo + 8);
-        }
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const int d = 32 * n + c32;
-          const FV v0 = *reinterpret_cast<const FV*>(v_lds + v_off(d, 4 * t + 2 * h0));
-          const FV v1 = *reinterpret_cast<const FV*>(v_lds + v_off(d, 4 * t + 2 * h0 + 1));
-          acc[n] = mfma32x32x16(v0, p0, acc[n]);
-          acc[n] = mfma32x32x16(v1, p1, acc[n]);
-          if constexpr (T::kSplitP) {
-            acc[n] = mfma32x32x16(v0, p0lo, acc[n]);
-            acc[n] = mfma32x32x16(v1, p1lo, acc[n]);
-          }
+          // the rounded pair as floats: bf16 bits are the top half of fp32
+          typedef __attribute__((__vector_size__(2 * sizeof(VOp)))) VOp VOpx2;
+          const VOpx2 hp = {ha, hb};
+          const uint32_t bits = __builtin_bit_cast(uint32_t, hp);
+          const float fa = __uint_as_float(bits << 16), fb = __uint_as_float(bits & 0xffff0000u);
+          out.lo[h][e] = (VOp)(a - fa);
+          out.lo[h][e + 1] = (VOp)(b - fb);
         }
       }
     }
+    return any;
+  };
 
-    if (st + 1 < nst) {
-      STG::commit(regs, st + 1, kv_len, k_nxt, v_nxt, wave, lane);
-      a0 = n0; a1 = n1; a2 = n2; a3 = n3;
+  // ---- pipeline ----
+  // Sub-tile j (keys 32j .. 32j+31) belongs to stage j/2. Step j first reads
+  // from LDS the V operands of sub-tile j and the K operands of sub-tile j+2,
+  // then turns S(j+1) into P(j+1) on the vector units while those reads are in
+  // flight, and only then issues the 24 matrix products PV(j) and
+  // S(j+2) = QK(j+2) back to back. The score product thus runs two sub-tiles
+  // ahead of the value product, and the two waves of a SIMD can overlap one's
+  // softmax with the other's products.
+  // K stage s and V stage s live in buffers s % kRing. During stage X the
+  // waves read K stage X+1 and V stage X; at its end (barrier B_X) K stage
+  // X+2 and V stage X+1 must have landed, and the freed buffers receive K
+  // stage X+kKAhead and V stage X+kVAhead. Direct-to-LDS loads keep three
+  // stages in flight; fp8 stages wait in registers, so they run one stage
+  // ahead.
+  constexpr int kKAhead = T::kFp8 ? 3 : kRing + 1;
+  constexpr int kVAhead = kKAhead - 1;
+  // vector-memory instructions one stage issues per wave (direct loads)
+  constexpr int kPerStage = T::kFp8 ? 0 : Dma<D, BLK>::kKInst + Dma<D, BLK>::kVInst;
+  PFrag<FV> pa, pb;  // P of sub-tiles 2X (pa) and 2X+1 (pb)
+  f32x16 sc;         // S of the next sub-tile to turn into P
+
+  auto lgkm_barrier = [&]() {  // LDS reads of this wave done, then meet the others
+    __builtin_amdgcn_s_waitcnt((0xF) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+  };
+  // B_X: this wave's loads of the stages needed next have landed (all but
+  // those of the last two issue points, when both were complete) and its LDS
+  // reads are done; then meet the other waves
+  auto ring_barrier = [&](bool keep_two) {
+    if constexpr (!T::kFp8) {
+      static_assert(2 * kPerStage < 16, "vmcnt field");
+      if (keep_two) __builtin_amdgcn_s_waitcnt((2 * kPerStage) | (7 << 4));  // vmcnt(2*kPerStage) lgkmcnt(0)
+      else __builtin_amdgcn_s_waitcnt(7 << 4);                                // vmcnt(0) lgkmcnt(0)
+    } else {
+      __builtin_amdgcn_s_waitcnt(7 << 4);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct-to-LDS loads of the next stage have landed
-    __syncthreads();
-    if constexpr (T::kDirect) {
-      if (tail_stage_exists && st + 2 == nst) {  // the next stage holds kv_len: clear dead values
-        STG::zero_tail(st + 1, kv_len, v_nxt, tid);
-        __syncthreads();
-      }
+    __builtin_amdgcn_s_barrier();
+  };
+
+  // prologue: K stages 0, 1 and V stage 0 loaded and awaited together with
+  // the Q fragments (one full wait, so that no load of the Q registers is left
+  // outstanding inside the loop); then K stages 2 .. kKAhead-2 and V stages
+  // 1 .. kVAhead-2 issued, P(0) and S(1) computed, and K stage kKAhead-1 and
+  // V stage kVAhead-1 issued once every wave has read K stage 0.
+  Ids ids0 = load_ids<BLK>(bt, 0, last_blk, p.num_blocks);
+  Ids ids1 = load_ids<BLK>(bt, 1, last_blk, p.num_blocks);
+  issue_k(0, ids0);
+  issue_v(0, ids0);
+  commit(0, 0);
+  if (nst > 1) {
+    issue_k(1, ids1);
+    commit(1, -1);
+  }
+  __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0) lgkmcnt(0)
+  Ids idsv = ids1;                     // V stage s-1 goes with K stage s
+#pragma unroll
+  for (int s2 = 2; s2 < kKAhead - 1; ++s2) {  // direct loads only (fp8: kKAhead - 1 == 2)
+    const Ids idsk = load_ids<BLK>(bt, s2, last_blk, p.num_blocks);
+    if (s2 < nst) issue_k(s2, idsk);
+    if (s2 - 1 < nst) issue_v(s2 - 1, idsv);
+    idsv = idsk;
+  }
+  lgkm_barrier();
+  if (nsub > 0) {
+    KOps k0;
+    load_k(0, 0, k0);
+    sc = qk(k0);
+    float alpha;
+    softmax(sc, 0, 32 > full_keys_w, pa, alpha);  // the accumulators are still zero
+  }
+  if (nsub > 1) {
+    KOps k1;
+    load_k(0, 1, k1);
+    sc = qk(k1);
+  }
+  lgkm_barrier();  // K stage 0 has been read: its buffer takes K stage kKAhead-1
+  Ids idsk = load_ids<BLK>(bt, kKAhead - 1, last_blk, p.num_blocks);
+  int pend_k = -1, pend_v = -1;  // fp8 stages waiting in registers
+  if (kKAhead - 1 < nst) {
+    issue_k(kKAhead - 1, idsk);
+    pend_k = kKAhead - 1;
+  }
+  if (kVAhead - 1 < nst) {
+    issue_v(kVAhead - 1, idsv);
+    pend_v = kVAhead - 1;
+  }
+  idsv = idsk;                                                 // V stage X+kVAhead at B_X
+  idsk = load_ids<BLK>(bt, kKAhead, last_blk, p.num_blocks);  // K stage X+kKAhead at B_X
+
+  // step j (every branch is uniform over the wave): PV(j) with pcur,
+  // P(j+1) = softmax(S(j+1)) into pnext, S(j+2) = QK(j+2)
+  auto step = [&](int j, int bk, int bv, int t, const PFrag<FV>& pcur, PFrag<FV>& pnext) {
+    const bool do_pv = j < nsub, do_sm = j + 1 < nsub, do_qk = j + 2 < nsub;
+    VOps vo;
+    KOps ko;
+    if (do_pv) load_v(bv, t, vo);
+    if (do_qk) load_k(bk, t, ko);
+    float alpha = 1.f;
+    bool rescale = false;
+    if (do_sm) rescale = softmax(sc, 32 * (j + 1), 32 * (j + 2) > full_keys_w, pnext, alpha);
+    if (do_pv) {
+      if (32 * (j + 1) > kv_len) zero_tail(vo, 32 * j);
+      pv(vo, pcur);
     }
+    if (rescale) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+    }
+    if (do_qk) sc = qk(ko);
+  };
+  for (int X = 0; X < nst; ++X) {
+    const int bv = X % kRing, bk = (X + 1) % kRing;
+    step(2 * X, bk, bv, 0, pa, pb);
+    step(2 * X + 1, bk, bv, 1, pb, pa);
+    // B_X
+    commit(pend_k, pend_v);
+    ring_barrier(X + kKAhead - 1 < nst);
+    pend_k = X + kKAhead < nst ? X + kKAhead : -1;
+    pend_v = X + kVAhead < nst ? X + kVAhead : -1;
+    if (X + kKAhead < nst) issue_k(X + kKAhead, idsk);
+    if (X + kVAhead < nst) issue_v(X + kVAhead, idsv);
+    idsv = idsk;
+    idsk = load_ids<BLK>(bt, X + kKAhead + 1, last_blk, p.num_blocks);
   }
 
   // ---- epilogue: O = O^T / l; element i of acc[n] is dim 32n + 8(i/4) + 4h0 + i%4 ----
-  l_run += __shfl_xor(l_run, 32);
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+    l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
   if (rvalid) {
     const float inv = p.v_scale / l_run;
     TQ* orow = reinterpret_cast<TQ*>(p.out) + (int64_t)(row_base + tok) * p.o_s0 + (int64_t)qh * p.o_s1;
