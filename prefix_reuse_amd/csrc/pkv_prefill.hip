@@ -105,11 +105,16 @@ __device__ __forceinline__ uint32_t lds_address(const char* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p);
 }
 
-template <typename TQ, typename TC>
+// kFast: a bf16 cache's values are converted to f16 in LDS (exact for
+// |v| < 65520, and f16 P carries 11 bits, as with an f16 cache); a work-group
+// that meets a larger or non-finite value redoes its rows without it.
+template <typename TQ, typename TC, bool kFast>
 struct Types {
   static constexpr bool kFp8 = std::is_same<TC, uint8_t>::value;
-  // PV operand type: the cache's own 16-bit type, f16 for an fp8 cache
-  typedef typename std::conditional<kFp8, f16_t, TC>::type VOp;
+  static constexpr bool kConvV = kFast && std::is_same<TC, bf16_t>::value;
+  // PV operand type: the cache's own 16-bit type, f16 for an fp8 cache or a
+  // converted bf16 one
+  typedef typename std::conditional<kFp8 || kConvV, f16_t, TC>::type VOp;
   static constexpr bool kSplitP = std::is_same<VOp, bf16_t>::value;
 };
 
@@ -253,9 +258,15 @@ struct PFrag {
   FV hi[2], lo[2];
 };
 
-template <typename TQ, typename TC, int D, int BLK>
-__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
-  typedef Types<TQ, TC> T;
+// LDS of a work-group: kRing K stages and kRing V stages, 16-bit elements
+template <int D>
+constexpr int kLdsBytes = kRing * 2 * kStage * D * 2;
+
+// The rows of one work-group. Returns false (having written nothing) when a
+// kFast pass met a value it cannot convert; the caller then runs the exact pass.
+template <typename TQ, typename TC, int D, int BLK, bool kFast>
+__device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg) {
+  typedef Types<TQ, TC, kFast> T;
   typedef typename T::VOp VOp;
   typedef typename Frag<TQ>::type F;
   typedef typename Frag<VOp>::type FV;
@@ -263,12 +274,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   constexpr int NT = D / 32;  // dim tiles of the output
   constexpr int kKBytes = kStage * D * (int)sizeof(TQ);
   constexpr int kVBytes = kStage * D * (int)sizeof(VOp);
-  __shared__ __attribute__((aligned(1024))) char lds[kRing * (kKBytes + kVBytes)];
+  static_assert(kRing * (kKBytes + kVBytes) == kLdsBytes<D>, "LDS budget");
   char* const k_lds0 = lds;                    // K stages: buffers 0 .. kRing-1
   char* const v_lds0 = lds + kRing * kKBytes;  // V stages: buffers 0 .. kRing-1
 
   // ---- which (KV head, request, row tile) ----
-  const int logical = xcd_remap(blockIdx.x, p.hkv * p.tiles_per_head);
+  const int logical = xcd_remap(wg, p.hkv * p.tiles_per_head);
   const int hk = logical / p.tiles_per_head;
   int tile = logical % p.tiles_per_head;
   int r = 0, row_base = 0, rows_r = 0;
@@ -282,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     tile -= nt;
     row_base += s;
   }
-  if (r >= p.num_reqs) return;
+  if (r >= p.num_reqs) return true;
   const int S = rows_r / p.group;
   int P = p.prefix_lens[r];
   P = P < 0 ? 0 : P;
@@ -307,7 +318,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   const int keys_w = wave_active ? min(kv_len, P + tok_last_w + 1) : 0;
   const int nsub = (keys_w + 31) / 32;                        // 32-key sub-tiles of this wave
   const int full_keys_w = min(P + tok_first_w + 1, kv_len);  // keys below need no mask in this wave
-  if (nst == 0) return;                                      // uniform over the work-group
+  if (nst == 0) return true;                                 // uniform over the work-group
 
   // ---- Q^T fragments for this lane's row ----
   const int row = wq0 + c32;
@@ -504,13 +515,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   // K stage s and V stage s live in buffers s % kRing. During stage X the
   // waves read K stage X+1 and V stage X; at its end (barrier B_X) K stage
   // X+2 and V stage X+1 must have landed, and the freed buffers receive K
-  // stage X+kKAhead and V stage X+kVAhead. Direct-to-LDS loads keep three
-  // stages in flight; fp8 stages wait in registers, so they run one stage
-  // ahead.
+  // stage X+kKAhead and V stage X+kVAhead (issued in that order: V, then K).
+  // Direct-to-LDS loads keep three stages in flight; fp8 stages wait in
+  // registers, so they run one stage ahead. A converted bf16 V stage must
+  // land one stage earlier: stage X converts V stage X+1 in place, and B_X
+  // publishes the result.
   constexpr int kKAhead = T::kFp8 ? 3 : kRing + 1;
   constexpr int kVAhead = kKAhead - 1;
-  // vector-memory instructions one stage issues per wave (direct loads)
-  constexpr int kPerStage = T::kFp8 ? 0 : Dma<D, BLK>::kKInst + Dma<D, BLK>::kVInst;
+  // vector-memory instructions a stage issues per wave (direct loads) and
+  // the number of them allowed to stay in flight at B_X
+  constexpr int kKI = T::kFp8 ? 0 : Dma<D, BLK>::kKInst;
+  constexpr int kVI = T::kFp8 ? 0 : Dma<D, BLK>::kVInst;
+  constexpr int kInFlight = T::kConvV ? 2 * kKI + kVI : 2 * kKI + 2 * kVI;
+  static_assert(kInFlight < 16, "vmcnt field");
   PFrag<FV> pa, pb;  // P of sub-tiles 2X (pa) and 2X+1 (pb)
   f32x16 sc;         // S of the next sub-tile to turn into P
 
@@ -519,24 +536,62 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     __builtin_amdgcn_s_barrier();
   };
   // B_X: this wave's loads of the stages needed next have landed (all but
-  // those of the last two issue points, when both were complete) and its LDS
-  // reads are done; then meet the other waves
-  auto ring_barrier = [&](bool keep_two) {
+  // those of the last issue points, when they were all made) and its LDS
+  // accesses are done; then meet the other waves
+  auto ring_barrier = [&](bool keep) {
     if constexpr (!T::kFp8) {
-      static_assert(2 * kPerStage < 16, "vmcnt field");
-      if (keep_two) __builtin_amdgcn_s_waitcnt((2 * kPerStage) | (7 << 4));  // vmcnt(2*kPerStage) lgkmcnt(0)
-      else __builtin_amdgcn_s_waitcnt(7 << 4);                                // vmcnt(0) lgkmcnt(0)
+      if (keep) __builtin_amdgcn_s_waitcnt(kInFlight | (7 << 4));  // vmcnt(kInFlight) lgkmcnt(0)
+      else __builtin_amdgcn_s_waitcnt(7 << 4);                     // vmcnt(0) lgkmcnt(0)
     } else {
       __builtin_amdgcn_s_waitcnt(7 << 4);
     }
     __builtin_amdgcn_s_barrier();
   };
 
+  // bf16 -> f16 in place for this thread's share of V stage `st`, tracking
+  // the largest |bf16| bit pattern among live keys (keys >= kv_len hold
+  // whatever the cache slots hold and are zeroed before use)
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 vmax = {0, 0};
+  auto convert_v = [&](int st) {
+    if constexpr (T::kConvV) {
+      constexpr int kPieces = kStage * D / 8;  // 16-byte pieces of a V stage
+      constexpr int kPpr = BLK / 8, kSh = kPpr == 2 ? 3 : 2;
+      char* vl = v_lds0 + (st % kRing) * kVBytes;
+      const bool tail = kStage * (st + 1) > kv_len;
+#pragma unroll
+      for (int i0 = 0; i0 < kPieces; i0 += kThreads) {
+        const int i = i0 + tid;
+        if (kPieces % kThreads != 0 && i >= kPieces) break;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(vl + i * 16);
+        u32x4 live = {~0u, ~0u, ~0u, ~0u};
+        if (tail) {
+          const int blk = i / (D * kPpr), rem = i % (D * kPpr);
+          const int d = rem / kPpr, slot = rem % kPpr;
+          const int k0 = kStage * st + blk * BLK + 8 * (slot ^ ((d >> kSh) & (kPpr - 1)));
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            live[e] = (k0 + 2 * e < kv_len ? 0xffffu : 0u) | (k0 + 2 * e + 1 < kv_len ? 0xffff0000u : 0u);
+        }
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t x = w[e];
+          vmax = __builtin_elementwise_max(vmax, __builtin_bit_cast(u16x2, x & 0x7fff7fffu & live[e]));
+          const f16x2 h = {(f16_t)__uint_as_float(x << 16), (f16_t)__uint_as_float(x & 0xffff0000u)};
+          o[e] = __builtin_bit_cast(uint32_t, h);
+        }
+        *reinterpret_cast<u32x4*>(vl + i * 16) = o;
+      }
+    }
+  };
+
   // prologue: K stages 0, 1 and V stage 0 loaded and awaited together with
   // the Q fragments (one full wait, so that no load of the Q registers is left
-  // outstanding inside the loop); then K stages 2 .. kKAhead-2 and V stages
-  // 1 .. kVAhead-2 issued, P(0) and S(1) computed, and K stage kKAhead-1 and
-  // V stage kVAhead-1 issued once every wave has read K stage 0.
+  // outstanding inside the loop) and V stage 0 converted; then V stages
+  // 1 .. kVAhead-2 and K stages 2 .. kKAhead-2 issued, P(0) and S(1)
+  // computed, and V stage kVAhead-1 and K stage kKAhead-1 issued once every
+  // wave has read K stage 0.
   Ids ids0 = load_ids<BLK>(bt, 0, last_blk, p.num_blocks);
   Ids ids1 = load_ids<BLK>(bt, 1, last_blk, p.num_blocks);
   issue_k(0, ids0);
@@ -547,12 +602,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     commit(1, -1);
   }
   __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0) lgkmcnt(0)
-  Ids idsv = ids1;                     // V stage s-1 goes with K stage s
+  convert_v(0);
+  Ids idsv = ids1;  // V stage s-1 goes with K stage s
 #pragma unroll
   for (int s2 = 2; s2 < kKAhead - 1; ++s2) {  // direct loads only (fp8: kKAhead - 1 == 2)
     const Ids idsk = load_ids<BLK>(bt, s2, last_blk, p.num_blocks);
-    if (s2 < nst) issue_k(s2, idsk);
     if (s2 - 1 < nst) issue_v(s2 - 1, idsv);
+    if (s2 < nst) issue_k(s2, idsk);
     idsv = idsk;
   }
   lgkm_barrier();
@@ -568,16 +624,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     load_k(0, 1, k1);
     sc = qk(k1);
   }
-  lgkm_barrier();  // K stage 0 has been read: its buffer takes K stage kKAhead-1
+  // B_{-1}: K stage 0 has been read (its buffer takes K stage kKAhead-1);
+  // a converted V stage 1 must have landed
+  ring_barrier(kKAhead - 2 < nst);
   Ids idsk = load_ids<BLK>(bt, kKAhead - 1, last_blk, p.num_blocks);
   int pend_k = -1, pend_v = -1;  // fp8 stages waiting in registers
-  if (kKAhead - 1 < nst) {
-    issue_k(kKAhead - 1, idsk);
-    pend_k = kKAhead - 1;
-  }
   if (kVAhead - 1 < nst) {
     issue_v(kVAhead - 1, idsv);
     pend_v = kVAhead - 1;
+  }
+  if (kKAhead - 1 < nst) {
+    issue_k(kKAhead - 1, idsk);
+    pend_k = kKAhead - 1;
   }
   idsv = idsk;                                                 // V stage X+kVAhead at B_X
   idsk = load_ids<BLK>(bt, kKAhead, last_blk, p.num_blocks);  // K stage X+kKAhead at B_X
@@ -605,6 +663,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   };
   for (int X = 0; X < nst; ++X) {
     const int bv = X % kRing, bk = (X + 1) % kRing;
+    if (X + 1 < nst) convert_v(X + 1);
     step(2 * X, bk, bv, 0, pa, pb);
     step(2 * X + 1, bk, bv, 1, pb, pa);
     // B_X
@@ -612,10 +671,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     ring_barrier(X + kKAhead - 1 < nst);
     pend_k = X + kKAhead < nst ? X + kKAhead : -1;
     pend_v = X + kVAhead < nst ? X + kVAhead : -1;
-    if (X + kKAhead < nst) issue_k(X + kKAhead, idsk);
     if (X + kVAhead < nst) issue_v(X + kVAhead, idsv);
+    if (X + kKAhead < nst) issue_k(X + kKAhead, idsk);
     idsv = idsk;
     idsk = load_ids<BLK>(bt, X + kKAhead + 1, last_blk, p.num_blocks);
+  }
+  if constexpr (T::kConvV) {
+    // a value the conversion could not keep: redo these rows exactly
+    const int big = max(vmax.x, vmax.y) >= 0x4780;  // |v| >= 65536 as bf16, inf or NaN
+    if (__syncthreads_or(big)) return false;
   }
 
   // ---- epilogue: O = O^T / l; element i of acc[n] is dim 32n + 8(i/4) + 4h0 + i%4 ----
@@ -637,6 +701,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         *reinterpret_cast<TQx4*>(orow + 32 * n + 8 * k + 4 * h0) = o;
       }
     }
+  }
+  return true;
+}
+
+template <typename TQ, typename TC, int D, int BLK>
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes<D>];
+  int wg = blockIdx.x;
+  if constexpr (std::is_same<TC, bf16_t>::value) {
+    if (!attend<TQ, TC, D, BLK, true>(p, lds, wg)) {
+      // rare: redo exactly. The empty asm hides that this pass works on the
+      // same work-group, so nothing computed for the fast pass is kept alive
+      // for it.
+      asm volatile("" : "+s"(wg));
+      attend<TQ, TC, D, BLK, false>(p, lds, wg);
+    }
+  } else {
+    attend<TQ, TC, D, BLK, false>(p, lds, wg);
   }
 }
 

@@ -96,3 +96,27 @@ def test_config4_reuse_equals_full_recompute_on_gpu():
     rows = [0, 1, 50, 98, 99]
     ref = oracle_prefill(full, rows=[1900 + r for r in rows])
     assert report("reuse-oracle", np64(out)[rows], ref[[1900 + r for r in rows]], torch.bfloat16, TOL[torch.bfloat16]) <= 1.0
+
+
+@pytest.mark.parametrize("big", [65280.0, 70000.0, -1.0e6])
+def test_prefill_bf16_large_values(big):
+    """bf16 values are converted to f16 for the value product when every live
+    value fits (65280 is the largest bf16 value below f16's overflow
+    threshold); a work-group that meets a larger one (70000, -1e6) redoes its
+    rows without the conversion. Either way the result matches the oracle.
+
+    Tolerance: an output is a convex combination of value rows and linear in
+    V, so the 2e-3 gate (stated for values of order 1) is applied to the
+    problem scaled by max|V|, i.e. 2e-3 * max|V| plus half an output ulp."""
+    print(f"prefill bf16 planted V value {big}", flush=True)
+    case = workloads.make_prefill_case(604, [40, 300, 7], [30, 60, 90], 8, 2, 128, 16, torch.bfloat16)
+    b = case.block_size
+    for r, t, h, d in ((0, 5, 0, 7), (1, 290, 1, 100)):  # live prefix tokens
+        blk = int(case.block_tables[r, t // b])
+        case.v_pool[blk, t % b, h, d] = big
+    case.v_new[12, 1, 3] = big  # a suffix token of request 0
+    run = gpu_prefill(case)
+    ref = oracle_prefill(case)
+    assert np.isfinite(np64(run.out)).all()
+    scale = max(1.0, abs(big))
+    assert report(f"big {big}", np64(run.out), ref, torch.bfloat16, TOL[torch.bfloat16] * scale) <= 1.0
