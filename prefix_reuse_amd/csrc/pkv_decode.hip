@@ -412,11 +412,29 @@ __global__ __launch_bounds__(kCombineHeads * D / 4) void decode_combine_kernel(D
   const int first = p.seq_info[2 * seq], n = p.seq_info[2 * seq + 1];
   if (n <= 1) return;
   const int64_t row0 = (int64_t)(first + seq) * p.hq + qh;  // slot of wave `first`
-  float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, p.ws_ml[(row0 + (int64_t)i * p.hq) * 2]);
-  float L = 0.f;
+  float M = -INFINITY, L = 0.f;
   f32x4 O = {0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < n; ++i) {
+  // one round of loads for up to kFew partials, then a general loop
+  constexpr int kFew = 8;
+  const int nf = n < kFew ? n : kFew;
+  f32x2 ml[kFew];
+  f32x4 o[kFew];
+#pragma unroll
+  for (int i = 0; i < kFew; ++i) {
+    const int64_t row = row0 + (int64_t)i * p.hq;
+    ml[i] = i < nf ? *reinterpret_cast<const f32x2*>(p.ws_ml + row * 2) : f32x2{-INFINITY, 0.f};
+    o[i] = i < nf ? *reinterpret_cast<const f32x4*>(p.ws_o + row * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int i = 0; i < kFew; ++i) M = fmaxf(M, ml[i][0]);
+  for (int i = kFew; i < n; ++i) M = fmaxf(M, p.ws_ml[(row0 + (int64_t)i * p.hq) * 2]);
+#pragma unroll
+  for (int i = 0; i < kFew; ++i) {
+    const float f = i < nf ? exp2f(ml[i][0] - M) : 0.f;
+    L += ml[i][1] * f;
+    O += o[i] * f;
+  }
+  for (int i = kFew; i < n; ++i) {
     const int64_t row = row0 + (int64_t)i * p.hq;
     const float f = exp2f(p.ws_ml[row * 2] - M);
     L += p.ws_ml[row * 2 + 1] * f;
