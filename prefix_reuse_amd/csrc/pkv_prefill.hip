@@ -101,6 +101,11 @@ __device__ __forceinline__ const char* uniform_ptr(const void* base, int64_t off
 __device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(lds), "v"(voff), "s"(base) : "memory", "m0");
 }
+// Work-group barrier that is also a compiler memory barrier: no LDS (or
+// other memory) access is moved across it, in either direction. Its wait is
+// the caller's explicit s_waitcnt, which the compiler's own wait insertion
+// sees and accounts for.
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 __device__ __forceinline__ uint32_t lds_address(const char* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p);
 }
@@ -453,7 +458,7 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
   // only when some row's max grows by more than 2^kLazy (rare); the factor
   // the accumulators then need is returned in `alpha` and applied by the
   // caller once the products of the previous sub-tile have been added.
-  auto softmax = [&](f32x16& sc, int key0, bool mask, PFrag<FV>& out, float& alpha) -> bool {
+  auto sm_max = [&](f32x16& sc, int key0, bool mask, float& alpha) -> bool {
     if (mask) {
       const int kb = key0 + 16 * h0;
 #pragma unroll
@@ -475,6 +480,9 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
       m_run = m_new;
       l_run *= alpha;
     }
+    return any;
+  };
+  auto sm_exp = [&](f32x16& sc, PFrag<FV>& out) {
     float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -501,6 +509,10 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
         }
       }
     }
+  };
+  auto softmax = [&](f32x16& sc, int key0, bool mask, PFrag<FV>& out, float& alpha) -> bool {
+    const bool any = sm_max(sc, key0, mask, alpha);
+    sm_exp(sc, out);
     return any;
   };
 
@@ -533,7 +545,7 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
 
   auto lgkm_barrier = [&]() {  // LDS reads of this wave done, then meet the others
     __builtin_amdgcn_s_waitcnt((0xF) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
+    block_barrier();
   };
   // B_X: this wave's loads of the stages needed next have landed (all but
   // those of the last issue points, when they were all made) and its LDS
@@ -545,7 +557,7 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     } else {
       __builtin_amdgcn_s_waitcnt(7 << 4);
     }
-    __builtin_amdgcn_s_barrier();
+    block_barrier();
   };
 
   // bf16 -> f16 in place for this thread's share of V stage `st`, tracking
@@ -602,6 +614,7 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     commit(1, -1);
   }
   __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0) lgkmcnt(0)
+  asm volatile("" ::: "memory");       // the stage's own loads have landed: no LDS access moves above
   convert_v(0);
   Ids idsv = ids1;  // V stage s-1 goes with K stage s
 #pragma unroll
@@ -661,12 +674,84 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     }
     if (do_qk) sc = qk(ko);
   };
-  for (int X = 0; X < nst; ++X) {
-    const int bv = X % kRing, bk = (X + 1) % kRing;
-    if (X + 1 < nst) convert_v(X + 1);
-    step(2 * X, bk, bv, 0, pa, pb);
-    step(2 * X + 1, bk, bv, 1, pb, pa);
-    // B_X
+  // A step away from the edges (no mask, no tail, every product present).
+  // Nothing of P(j+1) feeds PV(j) or S(j+2) = QK(j+2), so the row max of
+  // S(j+1) is taken between the value products and its exponentials between
+  // the score products, on the vector units while the matrix core works.
+  // vo, ko hold this step's operands; with `next`, the operands of sub-tile
+  // t+1 of the same stage are read into them once their products are issued.
+  // The order is fixed chunk by chunk: no instruction crosses a
+  // sched_barrier, and the empty asm statements keep each value computed in
+  // its chunk rather than next to its use.
+  auto step_full = [&](int bk, int bv, int t, const PFrag<FV>& pcur, PFrag<FV>& pnext, VOps& vo, KOps& ko,
+                       bool next) {
+    if constexpr (!T::kSplitP) {  // one value product per operand
+      constexpr int kE = 16 / (2 * NT);  // elements handled per value product
+      float mx = sc[0];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          acc[n] = mfma32x32x16(vo.v[u][n], pcur.hi[u], acc[n]);
+          const int i0 = (u * NT + n) * kE;
+#pragma unroll
+          for (int e = 0; e < kE; ++e) mx = fmaxf(mx, sc[i0 + e]);
+          asm volatile("" : "+v"(mx));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (next) load_v(bv, t + 1, vo);
+      __builtin_amdgcn_sched_barrier(0);
+      {  // the other 16 keys of this row sit in lane l ^ 32
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c2;  // scale > 0: max commutes
+      }
+      const bool grow = mx > m_run + kLazy;
+      const bool rescale = __any(grow);
+      float alpha = 1.f;
+      if (rescale) {
+        const float m_new = grow ? mx : m_run;
+        alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 for rows that keep their max
+        m_run = m_new;
+        l_run *= alpha;
+      }
+      // score products, each followed by 16/QS exponentials of P(j+1) and,
+      // with `next`, the read of the K operand it has just consumed
+      constexpr int kX = 16 / QS;
+      const char* kl_next = k_lds0 + bk * kKBytes + (t + 1) * kKSub;
+      f32x16 s2 = {};
+      float x[16];
+#pragma unroll
+      for (int c = 0; c < QS; ++c) {
+        s2 = mfma32x32x16(ko.k[c], qf[c], s2);
+#pragma unroll
+        for (int e = 0; e < kX; ++e) {
+          const int i = c * kX + e;
+          x[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], c2, -m_run));
+          asm volatile("" : "+v"(x[i]));
+        }
+        if (next) ko.k[c] = *reinterpret_cast<const F*>(kl_next + (kx ^ (c << 5)));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // row sum and packing of P(j+1)
+      float part[8];
+#pragma unroll
+      for (int pr = 0; pr < 8; ++pr) {  // elements 2pr, 2pr+1
+        const int h = pr / 4, e = 2 * (pr % 4);
+        pnext.hi[h][e] = (VOp)x[2 * pr];
+        pnext.hi[h][e + 1] = (VOp)x[2 * pr + 1];
+        part[pr] = x[2 * pr] + x[2 * pr + 1];
+      }
+      l_run += ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+      sc = s2;
+      if (rescale) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+      }
+    }
+  };
+  // B_X and the loads it frees buffers for
+  auto stage_end = [&](int X) {
     commit(pend_k, pend_v);
     ring_barrier(X + kKAhead - 1 < nst);
     pend_k = X + kKAhead < nst ? X + kKAhead : -1;
@@ -675,6 +760,37 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     if (X + kKAhead < nst) issue_k(X + kKAhead, idsk);
     idsv = idsk;
     idsk = load_ids<BLK>(bt, X + kKAhead + 1, last_blk, p.num_blocks);
+  };
+  // stages X < x_full have only full steps (sub-tiles up to 2X+3 exist in
+  // this wave and need no mask); they run in a loop of their own, so that
+  // neither loop carries the other's register needs
+  const int a_full = min(nsub - 1, full_keys_w / 32);
+  const int x_full = T::kSplitP ? 0 : __builtin_amdgcn_readfirstlane(a_full >= 3 ? (a_full - 3) / 2 + 1 : 0);
+  int X = 0;
+  for (; X < x_full; ++X) {
+    const int bv = X % kRing, bk = (X + 1) % kRing;
+    if (X + 1 < nst) convert_v(X + 1);
+    VOps vo;
+    KOps ko;
+    load_v(bv, 0, vo);
+    load_k(bk, 0, ko);
+    // fp8: the registers hold the staged loads, so sub-tile 1's operands are
+    // read only once sub-tile 0's products are done
+    constexpr bool kAhead = !T::kFp8;
+    step_full(bk, bv, 0, pa, pb, vo, ko, kAhead);
+    if (!kAhead) {
+      load_v(bv, 1, vo);
+      load_k(bk, 1, ko);
+    }
+    step_full(bk, bv, 1, pb, pa, vo, ko, false);
+    stage_end(X);
+  }
+  for (; X < nst; ++X) {
+    const int bv = X % kRing, bk = (X + 1) % kRing;
+    if (X + 1 < nst) convert_v(X + 1);
+    step(2 * X, bk, bv, 0, pa, pb);
+    step(2 * X + 1, bk, bv, 1, pb, pa);
+    stage_end(X);
   }
   if constexpr (T::kConvV) {
     // a value the conversion could not keep: redo these rows exactly
