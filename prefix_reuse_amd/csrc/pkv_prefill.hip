@@ -565,6 +565,13 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
   // whatever the cache slots hold and are zeroed before use)
   typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
   u16x2 vmax = {0, 0};
+  // two bf16 values (one word) -> two f16 values; `live` masks the halves
+  // that count towards the maximum
+  auto conv_word = [&](uint32_t x, uint32_t live) -> uint32_t {
+    vmax = __builtin_elementwise_max(vmax, __builtin_bit_cast(u16x2, x & 0x7fff7fffu & live));
+    const f16x2 h = {(f16_t)__uint_as_float(x << 16), (f16_t)__uint_as_float(x & 0xffff0000u)};
+    return __builtin_bit_cast(uint32_t, h);
+  };
   auto convert_v = [&](int st) {
     if constexpr (T::kConvV) {
       constexpr int kPieces = kStage * D / 8;  // 16-byte pieces of a V stage
@@ -587,12 +594,7 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
         }
         u32x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t x = w[e];
-          vmax = __builtin_elementwise_max(vmax, __builtin_bit_cast(u16x2, x & 0x7fff7fffu & live[e]));
-          const f16x2 h = {(f16_t)__uint_as_float(x << 16), (f16_t)__uint_as_float(x & 0xffff0000u)};
-          o[e] = __builtin_bit_cast(uint32_t, h);
-        }
+        for (int e = 0; e < 4; ++e) o[e] = conv_word(w[e], live[e]);
         *reinterpret_cast<u32x4*>(vl + i * 16) = o;
       }
     }
@@ -683,9 +685,18 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
   // The order is fixed chunk by chunk: no instruction crosses a
   // sched_barrier, and the empty asm statements keep each value computed in
   // its chunk rather than next to its use.
+  // A converted bf16 cache's V stage `cst` (the next one, no tail) is
+  // converted here too: the thread's piece t is read first, converted a word
+  // at a time between the score products and written back at the end.
   auto step_full = [&](int bk, int bv, int t, const PFrag<FV>& pcur, PFrag<FV>& pnext, VOps& vo, KOps& ko,
-                       bool next) {
+                       bool next, int cst) {
     if constexpr (!T::kSplitP) {  // one value product per operand
+      constexpr int kCP = kStage * D / 8 / kThreads;  // 16-byte pieces per thread and V stage
+      static_assert(kCP * kThreads * 8 == kStage * D, "whole pieces");
+      const bool conv = T::kConvV && t < kCP;
+      char* const cp = v_lds0 + (cst % kRing) * kVBytes + (t * kThreads + tid) * 16;
+      u32x4 cw = {};
+      if (conv) cw = *reinterpret_cast<const u32x4*>(cp);
       constexpr int kE = 16 / (2 * NT);  // elements handled per value product
       float mx = sc[0];
 #pragma unroll
@@ -731,8 +742,10 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
           asm volatile("" : "+v"(x[i]));
         }
         if (next) ko.k[c] = *reinterpret_cast<const F*>(kl_next + (kx ^ (c << 5)));
+        if (conv && c % (QS / 4) == QS / 4 - 1) cw[c / (QS / 4)] = conv_word(cw[c / (QS / 4)], ~0u);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (conv) *reinterpret_cast<u32x4*>(cp) = cw;
       // row sum and packing of P(j+1)
       float part[8];
 #pragma unroll
@@ -761,15 +774,18 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     idsv = idsk;
     idsk = load_ids<BLK>(bt, X + kKAhead + 1, last_blk, p.num_blocks);
   };
-  // stages X < x_full have only full steps (sub-tiles up to 2X+3 exist in
-  // this wave and need no mask); they run in a loop of their own, so that
-  // neither loop carries the other's register needs
+  // Stages X < x_full have only full steps: sub-tiles up to 2X+3 exist in
+  // this wave and need no mask (then X + 1 < nst, since nsub <= 2 nst), and
+  // stage X+1 has no key at or beyond kv_len, so its conversion needs no mask
+  // either. They run in a loop of their own, so that neither loop carries the
+  // other's register needs.
   const int a_full = min(nsub - 1, full_keys_w / 32);
-  const int x_full = T::kSplitP ? 0 : __builtin_amdgcn_readfirstlane(a_full >= 3 ? (a_full - 3) / 2 + 1 : 0);
+  const int x_full = T::kSplitP ? 0
+                                : __builtin_amdgcn_readfirstlane(
+                                      min(a_full >= 3 ? (a_full - 3) / 2 + 1 : 0, max(kv_len / kStage - 1, 0)));
   int X = 0;
   for (; X < x_full; ++X) {
     const int bv = X % kRing, bk = (X + 1) % kRing;
-    if (X + 1 < nst) convert_v(X + 1);
     VOps vo;
     KOps ko;
     load_v(bv, 0, vo);
@@ -777,12 +793,12 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     // fp8: the registers hold the staged loads, so sub-tile 1's operands are
     // read only once sub-tile 0's products are done
     constexpr bool kAhead = !T::kFp8;
-    step_full(bk, bv, 0, pa, pb, vo, ko, kAhead);
+    step_full(bk, bv, 0, pa, pb, vo, ko, kAhead, X + 1);
     if (!kAhead) {
       load_v(bv, 1, vo);
       load_k(bk, 1, ko);
     }
-    step_full(bk, bv, 1, pb, pa, vo, ko, false);
+    step_full(bk, bv, 1, pb, pa, vo, ko, false, X + 1);
     stage_end(X);
   }
   for (; X < nst; ++X) {
