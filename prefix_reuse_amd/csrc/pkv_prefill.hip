@@ -125,24 +125,27 @@ struct Types {
 
 // Physical block ids of the kStage/BLK blocks of one stage (plain ints:
 // arrays here end up in scratch). Scalar loads; entries past the last live
-// block repeat it.
+// block repeat it. load_ids_raw only issues the loads, so that their latency
+// can pass under a barrier's wait; clamp_ids then bounds the ids to the pool.
 struct Ids {
   int b0, b1, b2, b3;
 };
 template <int BLK>
-__device__ __forceinline__ Ids load_ids(const int32_t* bt, int st, int last, int num_blocks) {
+__device__ __forceinline__ Ids load_ids_raw(const int32_t* bt, int st, int last) {
   constexpr int kB = kStage / BLK;
   const sconst_i32* t = (const sconst_i32*)bt;
-  auto id = [&](int i) {
-    const int v = t[min(st * kB + i, last)];
-    return min(max(v, 0), num_blocks - 1);
-  };
-  Ids r;
-  r.b0 = id(0);
-  r.b1 = id(1);
-  r.b2 = kB == 4 ? id(2) : 0;
-  r.b3 = kB == 4 ? id(3) : 0;
-  return r;
+  int v[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < kB; ++i) v[i] = t[min(st * kB + i, last)];
+  return Ids{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ Ids clamp_ids(Ids r, int num_blocks) {
+  auto c = [&](int v) { return min(max(v, 0), num_blocks - 1); };
+  return Ids{c(r.b0), c(r.b1), c(r.b2), c(r.b3)};
+}
+template <int BLK>
+__device__ __forceinline__ Ids load_ids(const int32_t* bt, int st, int last, int num_blocks) {
+  return clamp_ids(load_ids_raw<BLK>(bt, st, last), num_blocks);
 }
 
 // 16-bit caches: every load is one wave-wide global_load_lds of 1 KB that
@@ -763,16 +766,18 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
       }
     }
   };
-  // B_X and the loads it frees buffers for
+  // B_X and the loads it frees buffers for (the ids of K stage X+kKAhead+1
+  // are fetched before the barrier's wait, which covers their latency)
   auto stage_end = [&](int X) {
     commit(pend_k, pend_v);
+    const Ids raw = load_ids_raw<BLK>(bt, X + kKAhead + 1, last_blk);
     ring_barrier(X + kKAhead - 1 < nst);
     pend_k = X + kKAhead < nst ? X + kKAhead : -1;
     pend_v = X + kVAhead < nst ? X + kVAhead : -1;
     if (X + kVAhead < nst) issue_v(X + kVAhead, idsv);
     if (X + kKAhead < nst) issue_k(X + kKAhead, idsk);
     idsv = idsk;
-    idsk = load_ids<BLK>(bt, X + kKAhead + 1, last_blk, p.num_blocks);
+    idsk = clamp_ids(raw, p.num_blocks);
   };
   // Stages X < x_full have only full steps: sub-tiles up to 2X+3 exist in
   // this wave and need no mask (then X + 1 < nst, since nsub <= 2 nst), and
