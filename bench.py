@@ -58,28 +58,26 @@ def load_traffic(name: str, files) -> dict | None:
     return rec
 
 
-class EventTimer:
-    """Average duration of repeated launches, measured with HIP events recorded
-    on the stream the kernels are launched on."""
+def warm_clocks(torch, fn, seconds=0.5):
+    """Untimed launches for a fixed wall time, so that the timed region does
+    not start on a GPU still raising its clocks."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
 
-    def __init__(self, torch, stream, n):
-        self.torch = torch
-        self.stream = stream
-        self.pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                      for _ in range(n)]
-        self.i = 0
 
-    def __enter__(self):
-        self.pairs[self.i][0].record(self.stream)
-        return self
-
-    def __exit__(self, *exc):
-        self.pairs[self.i][1].record(self.stream)
-        self.i += 1
-
-    def mean_ms(self) -> float:
-        self.torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in self.pairs[: self.i]) / max(self.i, 1)
+def time_launches(torch, stream, fn, n) -> float:
+    """Average milliseconds per launch of fn over n back-to-back launches,
+    from HIP events recorded on the launch stream around the whole region."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
 
 
 def decode_setup(torch, pkv, workloads, dev):
@@ -94,6 +92,8 @@ def decode_setup(torch, pkv, workloads, dev):
     need = pkv.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim,
                                       case.block_tables.shape[1], case.block_size)
     t["ws"] = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+    pkv.append(t["k_new"], t["v_new"], t["slots"], kc, vc)  # the newest token, as a step does
+    torch.cuda.synchronize()
     return t
 
 
@@ -106,6 +106,10 @@ def prefill_setup(torch, pkv, workloads, dev):
         "k_new": case.k_new.to(dev), "v_new": case.v_new.to(dev), "slots": case.slot_mapping.to(dev),
     }
     t["out"] = torch.empty_like(t["q"])
+    # the suffix K/V go into the cache first, as in the pages' flow (the slots
+    # hold the pool's NaN poison until then)
+    pkv.append(t["k_new"], t["v_new"], t["slots"], kc, vc)
+    torch.cuda.synchronize()
     return t
 
 
@@ -213,7 +217,7 @@ def cpu_baseline(case, min_seconds=10.0, max_seconds=30.0) -> dict:
 
 
 def ingest_profile(name: str, trace_dir: str, fetch_dir: str, write_dir: str, kernel_regex: str,
-                   command: str) -> None:
+                   command: str, last: int = 20) -> None:
     """Summarise rocprofv3 csv output (a kernel-trace --stats run and two
     --pmc runs, FETCH_SIZE then WRITE_SIZE) into profiles/<name>.md and
     profiles/<name>_traffic.json. Counters are calibrated by the 1 GiB device
@@ -230,6 +234,13 @@ def ingest_profile(name: str, trace_dir: str, fetch_dir: str, write_dir: str, ke
         return hits[0]
 
     stats = list(csv.DictReader(open(find(trace_dir, "kernel_stats.csv"))))
+    # the measured launches: the last `last` dispatches of each matched kernel
+    trace = list(csv.DictReader(open(find(trace_dir, "kernel_trace.csv"))))
+    by_kernel = {}
+    for r in sorted(trace, key=lambda r: int(r["Start_Timestamp"])):
+        if rx.search(r["Kernel_Name"]):
+            by_kernel.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    measured_ns = sum(sum(v[-last:]) / len(v[-last:]) for v in by_kernel.values())
     lines = [f"# {name}", "", "rocprofv3 summaries (MI355X, gfx950). Commands, run from /tmp with TMPDIR=/tmp:", "",
              "```", command, "```", "", "## Kernel trace (--kernel-trace --stats)", "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
@@ -263,12 +274,16 @@ def ingest_profile(name: str, trace_dir: str, fetch_dir: str, write_dir: str, ke
             total_bytes += v * factor * 1024
             parts[f"{label}:{k[:60]}"] = round(v * factor * 1024)
             lines.append(f"| {label} | {copy_kib:.0f} | {factor:.3f} | `{k[:60]}` | {v:.0f} | {mb:.2f} |")
-    lines += ["", f"Sum over the matched kernels: average duration {total_avg_ns/1e3:.2f} us per launch, "
-              f"HBM traffic {total_bytes/1e6:.2f} MB per launch.", ""]
+    lines += ["", "## Measured launches", "",
+              f"Average over the last {last} launches of each matched kernel (the ones after the clock warm-up, "
+              f"as timed in the benchmark): {measured_ns/1e3:.2f} us per launch (sum over the matched kernels); "
+              f"over all launches, warm-up included: {total_avg_ns/1e3:.2f} us.", "",
+              f"Sum over the matched kernels: HBM traffic {total_bytes/1e6:.2f} MB per launch.", ""]
     (ROOT / "profiles").mkdir(exist_ok=True)
     (ROOT / "profiles" / f"{name}.md").write_text("\n".join(lines))
     rec = {"name": name, "kernel_regex": kernel_regex, "sources_hash": sources_hash(KERNEL_SOURCES),
-           "avg_launch_us": round(total_avg_ns / 1e3, 3), "bytes_per_launch": round(total_bytes),
+           "avg_launch_us": round(measured_ns / 1e3, 3), "avg_launch_us_all": round(total_avg_ns / 1e3, 3),
+           "bytes_per_launch": round(total_bytes),
            "parts": parts, "command": command}
     (ROOT / "profiles" / f"{name}_traffic.json").write_text(json.dumps(rec, indent=1) + "\n")
     print(f"wrote profiles/{name}.md and profiles/{name}_traffic.json")
@@ -287,9 +302,10 @@ def main() -> int:
     ap.add_argument("--ingest-profile", nargs=5, metavar=("NAME", "TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "KERNEL_REGEX"),
                     help="summarise rocprofv3 csv output into profiles/ (no GPU needed)")
     ap.add_argument("--profile-command", default="", help="command text recorded with --ingest-profile")
+    ap.add_argument("--ingest-last", type=int, default=20, help="measured launches per kernel in the trace")
     args = ap.parse_args()
     if args.ingest_profile:
-        ingest_profile(*args.ingest_profile, command=args.profile_command)
+        ingest_profile(*args.ingest_profile, command=args.profile_command, last=args.ingest_last)
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -310,7 +326,10 @@ def main() -> int:
         call = {"decode": run_decode_call, "prefill": run_prefill_call,
                 "long": lambda pkv, t: run_long_context_decode(pkv, t, t["layers"][0])}[args.only]
         t = setup(torch, pkv, workloads, dev) if args.only != "long" else setup(torch, pkv, workloads, dev, 1)
-        for _ in range(args.warmup + args.steps):
+        for _ in range(args.warmup):
+            call(pkv, t)
+        warm_clocks(torch, lambda: call(pkv, t))
+        for _ in range(args.steps):  # the last `steps` launches are the measured ones
             call(pkv, t)
         torch.cuda.synchronize()
         # a plain copy of known size, to calibrate the memory counters
@@ -318,7 +337,7 @@ def main() -> int:
         b = torch.empty_like(a)
         b.copy_(a)
         torch.cuda.synchronize()
-        print(json.dumps({"only": args.only, "launches": args.warmup + args.steps, "copy_bytes": 1 << 30}))
+        print(json.dumps({"only": args.only, "measured_launches": args.steps, "copy_bytes": 1 << 30}))
         return 0
 
     # ---------------- decode step: append + decode ----------------
@@ -331,7 +350,7 @@ def main() -> int:
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
+    warm_clocks(torch, step)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     w0 = time.perf_counter()
     e0.record(stream)
@@ -344,12 +363,8 @@ def main() -> int:
     kv_bytes = case.kv_read_bytes()
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # the decode kernel alone: events around each launch on its stream
-    timer = EventTimer(torch, stream, args.steps)
-    for _ in range(args.steps):
-        with timer:
-            run_decode_call(pkv, t)
-    dec_ms = timer.mean_ms()
+    # the decode call alone (its two kernels), back to back on its stream
+    dec_ms = time_launches(torch, stream, lambda: run_decode_call(pkv, t), args.steps)
     dec_gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
     traffic = load_traffic("decode_llama3_8b_b64_fp16", KERNEL_SOURCES)
     roofline = {
@@ -382,14 +397,10 @@ def main() -> int:
         torch.cuda.empty_cache()
         p = prefill_setup(torch, pkv, workloads, dev)
         pc = p["case"]
-        pkv.append(p["k_new"], p["v_new"], p["slots"], p["kc"], p["vc"])
         for _ in range(args.warmup):
             run_prefill_call(pkv, p)
-        timer = EventTimer(torch, stream, args.steps)
-        for _ in range(args.steps):
-            with timer:
-                run_prefill_call(pkv, p)
-        pre_ms = timer.mean_ms()
+        warm_clocks(torch, lambda: run_prefill_call(pkv, p))
+        pre_ms = time_launches(torch, stream, lambda: run_prefill_call(pkv, p), args.steps)
         flops = pc.flops()
         tflops = flops / (pre_ms * 1e-3) / 1e12
         ptraffic = load_traffic("prefill_16x1900p100_bf16", KERNEL_SOURCES)
@@ -415,7 +426,7 @@ def main() -> int:
         lsteps = max(3, args.steps // 10)
         for _ in range(max(1, args.warmup // 5)):
             run_long_context_step(pkv, lt)
-        torch.cuda.synchronize()
+        warm_clocks(torch, lambda: run_long_context_step(pkv, lt), 0.3)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(lsteps):
@@ -424,12 +435,10 @@ def main() -> int:
         torch.cuda.synchronize()
         lms = e0.elapsed_time(e1) / lsteps
         lbytes = lc.kv_read_bytes_per_layer() * lc.num_layers
-        timer = EventTimer(torch, stream, lc.num_layers * lsteps)
-        for _ in range(lsteps):
-            for lay in lt["layers"]:
-                with timer:
-                    run_long_context_decode(pkv, lt, lay)
-        lay_ms = timer.mean_ms()
+        layers = lt["layers"]
+        it = iter(range(1 << 30))
+        lay_ms = time_launches(torch, stream, lambda: run_long_context_decode(pkv, lt, layers[next(it) % len(layers)]),
+                               lc.num_layers * lsteps)
         lay_gbs = lc.kv_read_bytes_per_layer() / (lay_ms * 1e-3) / 1e9
         ltraffic = load_traffic("decode_long_context_8x100k_fp8", KERNEL_SOURCES)
         result["long_context_fp8"] = {
