@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 typedef enum {
   PKV_F32 = 0,
@@ -84,7 +84,9 @@ typedef enum {
   PKV_ERR_LAYOUT = 4,      /* strides / alignment not supported */
   PKV_ERR_UNSUPPORTED = 5, /* head_dim, block size or head grouping not supported */
   PKV_ERR_WORKSPACE = 6,   /* decode workspace missing or too small */
-  PKV_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
+  PKV_ERR_HIP = 7,         /* the HIP runtime reported an error at launch */
+  PKV_ERR_NO_BLOCKS = 8,   /* prefix index: too few free or evictable blocks */
+  PKV_ERR_NOT_FOUND = 9    /* prefix index: unknown request or stored prefix */
 } pkv_status;
 
 /*

@@ -304,9 +304,10 @@ class RadixTree:
             x.lock += 1
 
     def unlock(self, tokens: Sequence[int], length: int) -> None:
-        for x in self._path_nodes(tokens, length):
-            if x.lock <= 0:
-                raise ValueError("unlock without lock")
+        path = self._path_nodes(tokens, length)
+        if any(x.lock <= 0 for x in path):
+            raise ValueError("unlock without lock")
+        for x in path:
             x.lock -= 1
 
     def _nodes(self) -> List[_Node]:

@@ -161,6 +161,16 @@ size_t decode_ws_bytes(int64_t num_seqs, int32_t hq, int32_t hkv, int32_t d, pkv
 
 }  // namespace
 
+namespace pkv {
+// status of the calls implemented in other sources (the prefix index): the
+// same thread-local message pkv_last_error() returns
+int record_status(int code, const char* msg) {
+  if (code == PKV_OK) g_error.clear();
+  else g_error = msg ? msg : "";
+  return code;
+}
+}  // namespace pkv
+
 extern "C" {
 
 int pkv_abi_version(void) { return PKV_ABI_VERSION; }

@@ -1,5 +1,5 @@
 """Host-only checks of the C ABI (no GPU needed): the library loads, exports
-every entry point include/pkv.h declares, and rejects bad arguments with a
+every entry point include/*.h declares, and rejects bad arguments with a
 status code and a message before launching anything."""
 import ctypes
 import re
@@ -10,14 +10,14 @@ import pytest
 import prefix_reuse_amd as pkv
 from prefix_reuse_amd import PkvTensor
 
-HEADER = Path(__file__).resolve().parent.parent / "include" / "pkv.h"
+HEADERS = sorted((Path(__file__).resolve().parent.parent / "include").glob("*.h"))
 
 F32, F16, BF16, FP8, I32, I64 = range(6)
 FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
 
 
 def declared_functions():
-    text = HEADER.read_text()
+    text = "\n".join(h.read_text() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
 
@@ -25,13 +25,13 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert {"pkv_append", "pkv_decode_attn", "pkv_suffix_prefill_attn", "pkv_decode_workspace_bytes",
-            "pkv_last_error", "pkv_abi_version"} <= set(names)
+            "pkv_last_error", "pkv_abi_version", "pkv_pc_admit", "pkv_radix_match"} <= set(names)
     for n in names:
         assert hasattr(pkv.lib, n), n
 
 
 def test_abi_version():
-    assert pkv.abi_version() == 1
+    assert pkv.abi_version() == 2
 
 
 def T(shape, dtype, strides=None, ptr=FAKE):
