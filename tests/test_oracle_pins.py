@@ -370,3 +370,40 @@ def test_chatbot_prefill_saving_arithmetic():
     with_reuse = g["prompt_tokens"]  # the prompt once, reused 999 times
     assert without == g["prefill_tokens_without_reuse"]
     assert round(100 * (1 - with_reuse / without)) >= g["saving_percent"]
+
+
+# ---------------------------------------------------------------- cascade decode
+def _grouped(seed, groups, dtype=torch.float32, hq=4, hkv=2, d=16, b=16):
+    case = workloads.make_grouped_decode_case(seed, groups, hq, hkv, d, b, dtype)
+    kc, vc = oracle.append(_np(case.k_pool), _np(case.v_pool), _np(case.k_new), _np(case.v_new),
+                           case.slot_mapping.numpy())
+    return case, kc, vc
+
+
+@pytest.mark.parametrize("groups", [
+    [([40, 70, 33], 32)],                          # one group, two shared blocks
+    [([40, 70, 33], 32), ([5], 0), ([100, 90], 64)],
+    [([20, 50], 48), ([0, 17], 16), ([16, 33], 16)],  # members shorter than / equal to the prefix, an empty one
+])
+def test_cascade_equals_decode_on_aliased_tables(groups):
+    case, kc, vc = _grouped(77, groups)
+    ref = oracle.decode_attention(_np(case.q), kc, vc, case.block_tables.numpy(), case.context_lens.numpy(),
+                                  case.scale)
+    got = oracle.cascade_decode_attention(_np(case.q), kc, vc, case.block_tables.numpy(),
+                                          case.context_lens.numpy(), case.meta["group_starts"].numpy(),
+                                          case.meta["shared_lens"].numpy(), case.scale)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_cascade_identical_shared_keys_give_mean_of_values():
+    # every key equal (shared and own): the softmax is uniform, out = mean of V
+    case, kc, vc = _grouped(5, [([48, 64, 80], 32)])
+    kc[:] = 0.3
+    ctx = case.context_lens.numpy()
+    got = oracle.cascade_decode_attention(_np(case.q), kc, vc, case.block_tables.numpy(), ctx,
+                                          case.meta["group_starts"].numpy(), case.meta["shared_lens"].numpy(),
+                                          case.scale)
+    for s in range(case.num_seqs):
+        vals = oracle.gather(vc, case.block_tables[s].numpy(), int(ctx[s]))
+        for h in range(case.num_q_heads):
+            np.testing.assert_allclose(got[s, h], vals[:, h // 2, :].mean(axis=0), rtol=0, atol=1e-12)

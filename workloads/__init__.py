@@ -221,6 +221,41 @@ def make_decode_case(seed: int, lens: List[int], num_q_heads: int, num_kv_heads:
         shared_blocks=n_shared, meta={"poison_block": poison, "seed": seed})
 
 
+def make_grouped_decode_case(seed: int, groups: List[tuple], num_q_heads: int, num_kv_heads: int,
+                             head_dim: int, block_size: int, dtype: torch.dtype,
+                             name: str = "grouped-decode") -> DecodeCase:
+    """Several groups of sequences, each group sharing its own prefix blocks:
+    ``groups`` is a list of (lens, shared_prefix_tokens) as for
+    make_decode_case. The groups' pools are laid side by side (block ids
+    offset), so blocks are shared within a group and never across groups.
+    meta["group_starts"] ([G+1]) and meta["shared_lens"] (per sequence, the
+    aliased whole blocks in tokens) describe the grouping."""
+    parts = [make_decode_case(seed * 1000 + i, list(lens), num_q_heads, num_kv_heads, head_dim, block_size,
+                              dtype, shared_prefix_tokens=shared)
+             for i, (lens, shared) in enumerate(groups)]
+    width = max(c.block_tables.shape[1] for c in parts)
+    offset, tables, starts, shared_lens = 0, [], [0], []
+    for c, (lens, shared) in zip(parts, groups):
+        bt = torch.full((c.num_seqs, width), c.meta["poison_block"], dtype=torch.int32)
+        bt[:, :c.block_tables.shape[1]] = c.block_tables
+        tables.append(bt + offset)
+        starts.append(starts[-1] + c.num_seqs)
+        shared_lens += [(shared // block_size) * block_size] * c.num_seqs
+        offset += c.num_blocks
+    slots, base = [], 0
+    for c in parts:
+        slots.append(torch.where(c.slot_mapping >= 0, c.slot_mapping + base * block_size, c.slot_mapping))
+        base += c.num_blocks
+    return DecodeCase(
+        name=name, dtype=dtype, block_size=block_size, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+        head_dim=head_dim, q=torch.cat([c.q for c in parts]), k_pool=torch.cat([c.k_pool for c in parts]),
+        v_pool=torch.cat([c.v_pool for c in parts]), block_tables=torch.cat(tables),
+        context_lens=torch.cat([c.context_lens for c in parts]), k_new=torch.cat([c.k_new for c in parts]),
+        v_new=torch.cat([c.v_new for c in parts]), slot_mapping=torch.cat(slots), scale=parts[0].scale,
+        meta={"group_starts": torch.tensor(starts, dtype=torch.int32),
+              "shared_lens": torch.tensor(shared_lens, dtype=torch.int32), "seed": seed})
+
+
 def make_prefill_case(seed: int, prefix_lens: List[int], suffix_lens: List[int], num_q_heads: int,
                       num_kv_heads: int, head_dim: int, block_size: int, dtype: torch.dtype,
                       name: str = "prefill", extra_free_blocks: int = 0,
