@@ -188,6 +188,55 @@ int pkv_suffix_prefill_attn(const pkv_tensor* q_suffix, const pkv_tensor* k_cach
                             float scale, float k_scale, float v_scale, const pkv_tensor* out,
                             void* stream);
 
+/*
+ * pkv_cascade_workspace_bytes — bytes of device workspace pkv_cascade_decode_attn
+ * needs on the CURRENT device: the decode workspace (rounded up to 16 bytes)
+ * plus, for the shared part, one partial result per (key chunk, sequence,
+ * query head): splits * num_seqs * H_q * (head_dim + 2) floats, where the
+ * shared keys are cut into splits = min(16, max(1, CUs / row tiles)) chunks so
+ * that the shared part fills the device (row tiles = H_kv * ceil(num_seqs * G
+ * / 256)). Returns 0 on invalid sizes.
+ */
+size_t pkv_cascade_workspace_bytes(int64_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim);
+
+/*
+ * pkv_cascade_decode_attn — one decode step for sequences that share prefix
+ * blocks, reading each shared block once per group instead of once per
+ * sequence.
+ * [A] §03: a common prefix is stored once and reused by every request that
+ * starts with it; [B] "RadixAttention": one system prompt shared by many chat
+ * requests; [C] §1, §3: the decode attention equation.
+ * The result is the one pkv_decode_attn computes for the same inputs:
+ * out[s, h] = softmax(scale * q[s,h] K_s^T) V_s over context_lens[s] tokens.
+ * It is computed in two parts merged by log-sum-exp: for each group, all
+ * queries of its sequences against its shared prefix at once (matrix cores),
+ * and for each sequence the tokens after the shared prefix.
+ *
+ *  q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
+ *  out           as for pkv_decode_attn; q and out must be f16 or bf16.
+ *  group_starts  [G + 1] int32, ascending, group_starts[0] = 0 and
+ *                group_starts[G] = num_seqs: group g is sequences
+ *                group_starts[g] .. group_starts[g+1] - 1.
+ *  shared_lens   [num_seqs] int32: tokens of the sequence's group prefix, the
+ *                same for every sequence of a group. The first
+ *                shared_lens[s] / B entries of the block tables of a group
+ *                must name the same blocks (a group of one with
+ *                shared_lens 0 is a plain decode). Lengths are rounded down to
+ *                whole blocks and cut to each sequence's context; the shared
+ *                part is read through the group's first sequence's table.
+ *  workspace     at least pkv_cascade_workspace_bytes(...) bytes, 16-byte
+ *                aligned; no initial contents needed; calls sharing one
+ *                workspace must be ordered on one stream.
+ * Inputs that break the group contract give unspecified results, but every
+ * access stays inside the caller's buffers.
+ */
+int pkv_cascade_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_tensor* v_cache,
+                            const pkv_tensor* block_tables, const pkv_tensor* context_lens,
+                            const pkv_tensor* group_starts, const pkv_tensor* shared_lens, float scale,
+                            float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                            const pkv_tensor* out, void* stream);
+
 /* Description of the last error on the calling thread ("" if none). The
  * pointer stays valid until the next pkv_* call on this thread. */
 const char* pkv_last_error(void);

@@ -21,6 +21,7 @@ import torch
 __all__ = [
     "LIB_PATH", "lib", "PkvError",
     "append", "decode_attn", "suffix_prefill_attn", "decode_workspace_bytes",
+    "cascade_decode_attn", "cascade_workspace_bytes",
     "empty_caches", "caches_from_logical", "k_logical", "v_logical", "abi_version",
 ]
 
@@ -66,6 +67,11 @@ def _load() -> ctypes.CDLL:
     L.pkv_suffix_prefill_attn.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_float,
                                           ctypes.c_float, P, ctypes.c_void_p]
     L.pkv_suffix_prefill_attn.restype = ctypes.c_int
+    L.pkv_cascade_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    L.pkv_cascade_workspace_bytes.restype = ctypes.c_size_t
+    L.pkv_cascade_decode_attn.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                          ctypes.c_void_p, ctypes.c_size_t, P, ctypes.c_void_p]
+    L.pkv_cascade_decode_attn.restype = ctypes.c_int
     L.pkv_last_error.argtypes = []
     L.pkv_last_error.restype = ctypes.c_char_p
     L.pkv_abi_version.argtypes = []
@@ -193,4 +199,29 @@ def suffix_prefill_attn(q_suffix: torch.Tensor, k_cache: torch.Tensor, v_cache: 
                                      float(scale), float(k_scale), float(v_scale), _ref(do),
                                      _stream(q_suffix.device))
     _check("pkv_suffix_prefill_attn", rc)
+    return out
+
+
+def cascade_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int) -> int:
+    return lib.pkv_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim)
+
+
+def cascade_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        block_tables: torch.Tensor, context_lens: torch.Tensor, group_starts: torch.Tensor,
+                        shared_lens: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
+                        k_scale: float = 1.0, v_scale: float = 1.0,
+                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode for groups of sequences sharing prefix blocks (the shared part is
+    read once per group); same result as ``decode_attn``."""
+    if out is None:
+        out = torch.empty_like(q)
+    need = cascade_workspace_bytes(q.shape[0], q.shape[1], k_cache.shape[1], q.shape[2])
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if (need and workspace is not None) else None
+    ws_bytes = workspace.numel() * workspace.element_size() if (need and workspace is not None) else 0
+    descs = list(map(_desc, (q, k_cache, v_cache, block_tables, context_lens, group_starts, shared_lens, out)))
+    rc = lib.pkv_cascade_decode_attn(*[_ref(d) for d in descs[:7]], float(scale), float(k_scale), float(v_scale),
+                                     ws_ptr, ws_bytes, _ref(descs[7]), _stream(q.device))
+    _check("pkv_cascade_decode_attn", rc)
     return out

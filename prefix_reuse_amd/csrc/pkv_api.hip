@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <string>
 
@@ -159,6 +160,31 @@ size_t decode_ws_bytes(int64_t num_seqs, int32_t hq, int32_t hkv, int32_t d, pkv
   return slots * hq * (size_t)(d + 2) * sizeof(float) + (size_t)num_seqs * 2 * sizeof(int32_t);
 }
 
+// cascade: how many work-groups share one row tile of the shared part, so
+// that the shared part fills the device (at most 16: the combine's limit)
+// PKV_CASCADE_SPLITS (1..16) forces the count.
+int cascade_splits(int64_t num_seqs, int32_t hq, int32_t hkv) {
+  if (const char* env = getenv("PKV_CASCADE_SPLITS")) {
+    const long forced = atol(env);
+    if (forced >= 1 && forced <= 16) return (int)forced;
+  }
+  constexpr int64_t W = pkv::kPrefillRowsPerWg;
+  const int64_t tiles = (int64_t)hkv * ((num_seqs * (hq / hkv) + W - 1) / W);
+  int64_t sp = device_cus() / (tiles > 0 ? tiles : 1);
+  return (int)(sp < 1 ? 1 : (sp > 16 ? 16 : sp));
+}
+
+// cascade: the decode workspace (rounded up to 16 bytes), then the shared
+// partials O [splits, S, Hq, d] and (m, l) [splits, S, Hq, 2]
+size_t cascade_ws_bytes(int64_t num_seqs, int32_t hq, int32_t hkv, int32_t d, pkv::DecodePlan* plan_out,
+                        size_t* shared_offset, int* splits_out) {
+  const size_t dec = (decode_ws_bytes(num_seqs, hq, hkv, d, plan_out) + 15) / 16 * 16;
+  const int splits = cascade_splits(num_seqs, hq, hkv);
+  if (shared_offset) *shared_offset = dec;
+  if (splits_out) *splits_out = splits;
+  return dec + (size_t)splits * num_seqs * hq * (size_t)(d + 2) * sizeof(float);
+}
+
 }  // namespace
 
 namespace pkv {
@@ -174,6 +200,115 @@ int record_status(int code, const char* msg) {
 extern "C" {
 
 int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+
+size_t pkv_cascade_workspace_bytes(int64_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim) {
+  if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 || head_dim < 1)
+    return 0;
+  return cascade_ws_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, nullptr, nullptr, nullptr);
+}
+
+int pkv_cascade_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_tensor* v_cache,
+                            const pkv_tensor* block_tables, const pkv_tensor* context_lens,
+                            const pkv_tensor* group_starts, const pkv_tensor* shared_lens, float scale,
+                            float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                            const pkv_tensor* out, void* stream) {
+  int rc;
+  CacheGeom cg;
+  if ((rc = check_caches(k_cache, v_cache, &cg))) return rc;
+  if ((rc = check_tensor(q, "q", 3))) return rc;
+  if ((rc = check_tensor(out, "out", 3))) return rc;
+  const int64_t S = q->shape[0], hq = q->shape[1];
+  if (q->shape[2] != cg.dim) return fail(PKV_ERR_SHAPE, "q head_dim %lld != cache head_dim %d", (long long)q->shape[2], cg.dim);
+  for (int i = 0; i < 3; ++i)
+    if (out->shape[i] != q->shape[i]) return fail(PKV_ERR_SHAPE, "out shape differs from q");
+  if (hq < 1 || hq % cg.hkv != 0) return fail(PKV_ERR_UNSUPPORTED, "H_q=%lld is not a multiple of H_kv=%d", (long long)hq, cg.hkv);
+  if (hq > INT32_MAX || S > INT32_MAX) return fail(PKV_ERR_SHAPE, "too many sequences or heads");
+  if (out->dtype != q->dtype) return fail(PKV_ERR_DTYPE, "out dtype must equal q dtype");
+  if (q->dtype != PKV_F16 && q->dtype != PKV_BF16)
+    return fail(PKV_ERR_DTYPE, "cascade decode needs q in f16 or bf16 (the shared part runs on matrix cores)");
+  const bool fp8 = cg.dtype == PKV_FP8_E4M3FN;
+  if (fp8) {
+    if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+      return fail(PKV_ERR_SHAPE, "fp8 cache needs finite positive k_scale and v_scale");
+  } else if (q->dtype != cg.dtype) {
+    return fail(PKV_ERR_DTYPE, "q is %s but the cache is %s", dtype_name(q->dtype), dtype_name(cg.dtype));
+  }
+  if ((rc = check_block_tables(block_tables, S))) return rc;
+  if ((rc = check_int_vector(context_lens, "context_lens", S))) return rc;
+  if ((rc = check_int_vector(shared_lens, "shared_lens", S))) return rc;
+  if ((rc = check_tensor(group_starts, "group_starts", 1))) return rc;
+  const int64_t G = group_starts->shape[0] - 1;
+  if (G < 0) return fail(PKV_ERR_SHAPE, "group_starts needs at least one entry");
+  if ((rc = check_int_vector(group_starts, "group_starts", G + 1))) return rc;
+  if (!std::isfinite(scale)) return fail(PKV_ERR_SHAPE, "scale must be finite");
+  if (S == 0) return ok();
+  if ((rc = check_rows(q, "q"))) return rc;
+  if ((rc = check_rows(out, "out"))) return rc;
+  if (S * (hq / cg.hkv) > INT32_MAX / 2 || G > INT32_MAX) return fail(PKV_ERR_SHAPE, "too many rows");
+
+  pkv::DecodePlan plan;
+  size_t sh_off = 0;
+  int splits = 1;
+  const size_t need = cascade_ws_bytes(S, (int32_t)hq, cg.hkv, cg.dim, &plan, &sh_off, &splits);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "cascade workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(PKV_ERR_LAYOUT, "workspace must be 16-byte aligned");
+  float* sh_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + sh_off);
+  float* sh_ml = sh_o + (size_t)splits * S * hq * cg.dim;
+  const float qk = scale * (fp8 ? k_scale : 1.0f) * pkv::kLog2eHost;
+
+  // 1. every group's queries over its shared prefix, once (matrix cores)
+  if (G > 0) {
+    pkv::PrefillParams sp{};
+    sp.q = q->data; sp.q_s0 = q->stride[0]; sp.q_s1 = q->stride[1];
+    sp.k_cache = k_cache->data; sp.v_cache = v_cache->data;
+    sp.block_tables = reinterpret_cast<const int32_t*>(block_tables->data);
+    sp.bt_s0 = block_tables->stride[0]; sp.max_blocks = (int32_t)block_tables->shape[1];
+    sp.num_reqs = (int32_t)G; sp.hq = (int32_t)hq; sp.hkv = cg.hkv; sp.group = (int32_t)(hq / cg.hkv);
+    sp.num_blocks = (int32_t)cg.num_blocks; sp.total_rows = S;
+    constexpr int64_t W = pkv::kPrefillRowsPerWg;
+    const int64_t tiles = ((S * sp.group + W - 1) / W + G) * splits;
+    if (tiles * cg.hkv > INT32_MAX) return fail(PKV_ERR_SHAPE, "problem too large for one launch");
+    sp.tiles_per_head = (int32_t)tiles;
+    sp.key_splits = splits;
+    sp.qk_scale_log2 = qk;
+    sp.v_scale = fp8 ? v_scale : 1.0f;
+    sp.group_starts = reinterpret_cast<const int32_t*>(group_starts->data);
+    sp.context_lens = reinterpret_cast<const int32_t*>(context_lens->data);
+    sp.shared_lens = reinterpret_cast<const int32_t*>(shared_lens->data);
+    sp.ws_o = sh_o;
+    sp.ws_ml = sh_ml;
+    hipError_t e = pkv::launch_prefill(sp, to_dt(q->dtype), to_dt(cg.dtype), cg.dim, cg.block, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "cascade shared-prefix launch failed: %s", hipGetErrorString(e));
+  }
+  // 2. each sequence's own tokens, then the merge with its shared partial
+  pkv::DecodeParams p{};
+  p.q = q->data; p.q_s0 = q->stride[0]; p.q_s1 = q->stride[1];
+  p.k_cache = k_cache->data; p.v_cache = v_cache->data;
+  p.block_tables = reinterpret_cast<const int32_t*>(block_tables->data);
+  p.bt_s0 = block_tables->stride[0]; p.max_blocks = (int32_t)block_tables->shape[1];
+  p.context_lens = reinterpret_cast<const int32_t*>(context_lens->data);
+  p.out = out->data; p.o_s0 = out->stride[0]; p.o_s1 = out->stride[1];
+  p.num_seqs = (int32_t)S; p.hq = (int32_t)hq; p.hkv = cg.hkv; p.group = (int32_t)(hq / cg.hkv);
+  p.head_chunks = (p.group + 15) / 16; p.num_blocks = (int32_t)cg.num_blocks;
+  p.waves_per_head = plan.waves_per_head;
+  p.total_wgs = plan.total_waves;
+  const size_t slots = (size_t)plan.waves_per_head + (size_t)S;
+  p.ws_o = reinterpret_cast<float*>(workspace);
+  p.ws_ml = p.ws_o + slots * hq * cg.dim;
+  p.seq_info = reinterpret_cast<int32_t*>(p.ws_ml + slots * hq * 2);
+  p.qk_scale_log2 = qk;
+  p.v_scale = fp8 ? v_scale : 1.0f;
+  p.shared_lens = reinterpret_cast<const int32_t*>(shared_lens->data);
+  p.sh_o = sh_o;
+  p.sh_ml = sh_ml;
+  p.sh_splits = splits;
+  hipError_t e = pkv::launch_decode(p, to_dt(q->dtype), to_dt(cg.dtype), cg.dim, cg.block, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "cascade decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
 
 const char* pkv_last_error(void) { return g_error.c_str(); }
 

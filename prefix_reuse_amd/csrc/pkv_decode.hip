@@ -160,6 +160,24 @@ __device__ __forceinline__ int ctx_of(const DecodeParams& p, int s, int cap) {
   return c < 0 ? 0 : (c > cap ? cap : c);
 }
 
+// Cascade decode: tokens of sequence s before this one belong to its group's
+// shared prefix (whole blocks, cut to its context); 0 for a plain decode.
+template <int BLK>
+__device__ __forceinline__ int shared_of(const DecodeParams& p, int s, int ctx) {
+  if (!p.shared_lens) return 0;
+  int l = p.shared_lens[s];
+  l = l < 0 ? 0 : l;
+  l -= l % BLK;  // whole blocks, then cut to the context (a short sequence ends inside them)
+  return l > ctx ? ctx : l;
+}
+
+// tokens the decode kernel covers: all of them, or those after the shared prefix
+template <int BLK>
+__device__ __forceinline__ int own_of(const DecodeParams& p, int s, int cap) {
+  const int c = ctx_of(p, s, cap);
+  return c - shared_of<BLK>(p, s, c);
+}
+
 // Wave-wide inclusive scan of one value per lane.
 __device__ __forceinline__ int wave_scan(int x, int lane) {
 #pragma unroll
@@ -192,7 +210,7 @@ __global__ __launch_bounds__(64, 3) void decode_kernel(DecodeParams p) {
   int total = 0;
   for (int b = 0; b < p.num_seqs; b += 64) {
     const int s = b + lane;
-    int ch = s < p.num_seqs ? (ctx_of(p, s, cap) + kChunk - 1) / kChunk : 0;
+    int ch = s < p.num_seqs ? (own_of<BLK>(p, s, cap) + kChunk - 1) / kChunk : 0;
     total += __shfl(wave_scan(ch, lane), 63);
   }
   total = __builtin_amdgcn_readfirstlane(total);
@@ -205,7 +223,7 @@ __global__ __launch_bounds__(64, 3) void decode_kernel(DecodeParams p) {
     int run = 0;
     for (int b = 0; b < p.num_seqs; b += 64) {
       const int s = b + lane;
-      int ch = s < p.num_seqs ? (ctx_of(p, s, cap) + kChunk - 1) / kChunk : 0;
+      int ch = s < p.num_seqs ? (own_of<BLK>(p, s, cap) + kChunk - 1) / kChunk : 0;
       const int incl = run + wave_scan(ch, lane);
       const int first = incl - ch;
       if (s < p.num_seqs) {
@@ -222,7 +240,7 @@ __global__ __launch_bounds__(64, 3) void decode_kernel(DecodeParams p) {
     int run = 0;
     for (int b = 0; b < p.num_seqs; b += 64) {
       const int s = b + lane;
-      int ch = s < p.num_seqs ? (ctx_of(p, s, cap) + kChunk - 1) / kChunk : 0;
+      int ch = s < p.num_seqs ? (own_of<BLK>(p, s, cap) + kChunk - 1) / kChunk : 0;
       const int incl = run + wave_scan(ch, lane);
       const unsigned long long hit = __ballot(s < p.num_seqs && incl > c0);
       if (hit) {
@@ -245,9 +263,13 @@ __global__ __launch_bounds__(64, 3) void decode_kernel(DecodeParams p) {
   QT qf[QS];
   f32x4 acc[NT];
   float m_run, l_run;
-  int ctx = ctx_of(p, s_cur, cap);
+  // ctx counts this kernel's tokens of s_cur; bt starts at the first of them
+  auto table_of = [&](int s) {
+    return p.block_tables + (int64_t)s * p.bt_s0 + shared_of<BLK>(p, s, ctx_of(p, s, cap)) / BLK;
+  };
+  int ctx = own_of<BLK>(p, s_cur, cap);
   int tb = (c0 - s_first_chunk) * kChunk;
-  const int32_t* bt = p.block_tables + (int64_t)s_cur * p.bt_s0;
+  const int32_t* bt = table_of(s_cur);
 
   auto start_seq = [&]() {
     load_q<TQ, TC, D>(qf, reinterpret_cast<const TQ*>(p.q) + s_cur * p.q_s0 + qh_lane * p.q_s1, hvalid, g);
@@ -372,15 +394,15 @@ __global__ __launch_bounds__(64, 3) void decode_kernel(DecodeParams p) {
     tb += kChunk;
     if (tb >= ctx || c + 1 == c1) {
       const int nch = (ctx + kChunk - 1) / kChunk;
-      finish_seq(seq_start >= c0 && seq_start + nch <= c1);
+      finish_seq(!p.shared_lens && seq_start >= c0 && seq_start + nch <= c1);  // cascade: always a partial
       if (c + 1 == c1) break;
       seq_start += nch;
       do {  // next non-empty sequence
         ++s_cur;
-        ctx = ctx_of(p, s_cur, cap);
+        ctx = own_of<BLK>(p, s_cur, cap);
       } while (ctx == 0);
       tb = 0;
-      bt = p.block_tables + (int64_t)s_cur * p.bt_s0;
+      bt = table_of(s_cur);
       start_seq();
     }
   }
@@ -402,18 +424,47 @@ __global__ __launch_bounds__(kCombineHeads * D / 4) void decode_combine_kernel(D
   const int cap = p.max_blocks * BLK;
   TQ* out = reinterpret_cast<TQ*>(p.out) + seq * p.o_s0 + qh * p.o_s1 + d0;
   typedef __attribute__((__vector_size__(4 * sizeof(TQ)))) TQ TQx4;
-  if (ctx_of(p, seq, cap) == 0) {
+  const int ctx = ctx_of(p, seq, cap);
+  if (ctx == 0) {
     TQx4 z;
 #pragma unroll
     for (int i = 0; i < 4; ++i) z[i] = from_f32<TQ>(0.f);
     *reinterpret_cast<TQx4*>(out) = z;
     return;
   }
-  const int first = p.seq_info[2 * seq], n = p.seq_info[2 * seq + 1];
-  if (n <= 1) return;
+  const int first = p.seq_info[2 * seq];
+  int n = p.seq_info[2 * seq + 1];
+  if (!p.shared_lens && n <= 1) return;
+  if (own_of<BLK>(p, seq, cap) == 0) n = 0;  // cascade, nothing after the shared prefix
   const int64_t row0 = (int64_t)(first + seq) * p.hq + qh;  // slot of wave `first`
   float M = -INFINITY, L = 0.f;
   f32x4 O = {0.f, 0.f, 0.f, 0.f};
+  // cascade: the shared prefix's partials (one per key chunk that reaches
+  // into this sequence's shared tokens) join the merge first
+  constexpr int kMaxSplits = 16;
+  f32x2 sml[kMaxSplits];
+  f32x4 so[kMaxSplits];
+  int nsh = 0;
+  if (p.shared_lens) {
+    const int sh = shared_of<BLK>(p, seq, ctx);
+    int lr = p.shared_lens[seq];
+    lr = lr < 0 ? 0 : lr;
+    lr -= lr % BLK;
+    const int chunk = cascade_chunk(lr, p.sh_splits);
+    nsh = chunk > 0 ? min((sh + chunk - 1) / chunk, min(p.sh_splits, kMaxSplits)) : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxSplits; ++i) {
+    sml[i] = f32x2{-INFINITY, 0.f};
+    so[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (i < nsh) {
+      const int64_t srow = ((int64_t)i * p.num_seqs + seq) * p.hq + qh;
+      sml[i] = *reinterpret_cast<const f32x2*>(p.sh_ml + srow * 2);
+      so[i] = *reinterpret_cast<const f32x4*>(p.sh_o + srow * D + d0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxSplits; ++i) M = fmaxf(M, sml[i][0]);
   // one round of loads for up to kFew partials, then a general loop
   constexpr int kFew = 8;
   const int nf = n < kFew ? n : kFew;
@@ -428,6 +479,12 @@ __global__ __launch_bounds__(kCombineHeads * D / 4) void decode_combine_kernel(D
 #pragma unroll
   for (int i = 0; i < kFew; ++i) M = fmaxf(M, ml[i][0]);
   for (int i = kFew; i < n; ++i) M = fmaxf(M, p.ws_ml[(row0 + (int64_t)i * p.hq) * 2]);
+#pragma unroll
+  for (int i = 0; i < kMaxSplits; ++i) {
+    const float f = i < nsh ? exp2f(sml[i][0] - M) : 0.f;
+    L += sml[i][1] * f;
+    O += so[i] * f;
+  }
 #pragma unroll
   for (int i = 0; i < kFew; ++i) {
     const float f = i < nf ? exp2f(ml[i][0] - M) : 0.f;

@@ -36,6 +36,14 @@ struct DecodeParams {
   int32_t total_wgs;                  // one wave per work-group
   float qk_scale_log2;                // softmax scale * k_scale * log2(e)
   float v_scale;
+  // cascade decode (nullptr otherwise): each sequence's shared-prefix length
+  // (rounded down to whole blocks, at most its context); the decode kernel
+  // covers only the tokens after it and writes every result as a partial,
+  // and the combine merges in the shared partial [S, Hq, D] / [S, Hq, 2]
+  const int32_t* shared_lens;
+  const float* sh_o;                  // [sh_splits, S, Hq, D]: one partial per key split
+  const float* sh_ml;                 // [sh_splits, S, Hq, 2]
+  int32_t sh_splits;
 };
 
 // Suffix-prefill work-group: kPrefillWaves waves of 32 (token, head) rows each.
@@ -53,7 +61,28 @@ struct PrefillParams {
   int32_t tiles_per_head;             // grid size / hkv (upper bound on tiles)
   float qk_scale_log2;
   float v_scale;
+  // cascade decode's shared part (group_starts == nullptr otherwise): the
+  // "requests" are groups of sequences group_starts[g] .. group_starts[g+1]-1,
+  // one query row per (sequence, head), attending to the group's shared
+  // prefix (shared_lens of its first sequence, whole blocks, read through
+  // that sequence's block table) up to each sequence's own context length;
+  // unnormalised partials go to ws_o [S, Hq, D] and ws_ml [S, Hq, 2]
+  const int32_t* group_starts;
+  const int32_t* context_lens;
+  const int32_t* shared_lens;
+  float* ws_o;                        // [key_splits, S, Hq, D]
+  float* ws_ml;                       // [key_splits, S, Hq, 2]
+  int32_t key_splits;                 // work-groups sharing one row tile's shared keys
 };
+
+// Cascade decode: the shared keys of a group (L, whole blocks) are cut into
+// `splits` chunks of whole 64-key stages; chunk i covers keys
+// [i * chunk, min(L, (i + 1) * chunk)).
+constexpr int kCascadeChunkAlign = 64;
+__host__ __device__ inline int cascade_chunk(int L, int splits) {
+  const int c = (L + splits - 1) / splits;
+  return (c + kCascadeChunkAlign - 1) / kCascadeChunkAlign * kCascadeChunkAlign;
+}
 
 // Decode launch plan shared by the launcher and the workspace-size query.
 struct DecodePlan { int32_t waves_per_head; int32_t total_waves; };

@@ -290,9 +290,17 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
   const int logical = xcd_remap(wg, p.hkv * p.tiles_per_head);
   const int hk = logical / p.tiles_per_head;
   int tile = logical % p.tiles_per_head;
+  // cascade decode's shared part: the requests are groups of sequences, and
+  // key_splits work-groups share a row tile, each on one chunk of the keys
+  const bool casc = p.group_starts != nullptr;
+  int split = 0;
+  if (casc) {
+    split = tile % p.key_splits;
+    tile /= p.key_splits;
+  }
   int r = 0, row_base = 0, rows_r = 0;
   for (; r < p.num_reqs; ++r) {
-    int s = p.suffix_lens[r];
+    int s = casc ? p.group_starts[r + 1] - p.group_starts[r] : p.suffix_lens[r];
     s = s < 0 ? 0 : s;
     if (row_base + s > p.total_rows) s = (int)(p.total_rows - row_base);
     rows_r = s * p.group;
@@ -303,12 +311,24 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
   }
   if (r >= p.num_reqs) return true;
   const int S = rows_r / p.group;
-  int P = p.prefix_lens[r];
-  P = P < 0 ? 0 : P;
   const int cap = p.max_blocks * BLK;
-  int kv_len = P + S;
-  if (kv_len > cap) kv_len = cap;
-  const int32_t* bt = p.block_tables + (int64_t)r * p.bt_s0;
+  int P, kv_len, k0 = 0;
+  const int32_t* bt;
+  if (casc) {  // the group's shared prefix, whole blocks, through its first sequence's table
+    P = p.shared_lens[row_base];
+    P = P < 0 ? 0 : (P > cap ? cap : P);
+    P -= P % BLK;
+    const int chunk = cascade_chunk(P, p.key_splits);
+    k0 = split * chunk;  // this work-group's keys: k0 .. k0 + kv_len - 1
+    kv_len = max(min(P - k0, chunk), 0);
+    bt = p.block_tables + (int64_t)row_base * p.bt_s0 + (kv_len > 0 ? k0 / BLK : 0);
+  } else {
+    P = p.prefix_lens[r];
+    P = P < 0 ? 0 : P;
+    kv_len = P + S;
+    if (kv_len > cap) kv_len = cap;
+    bt = p.block_tables + (int64_t)r * p.bt_s0;
+  }
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -321,12 +341,23 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
   const int tok_first_w = wq0 / p.group;
   const int tok_last_w = min(S - 1, (wq0 + kRowsWave - 1) / p.group);
   const bool wave_active = wq0 < rows_r;
-  const int keys_wg = min(kv_len, P + tok_last_wg + 1);
+  // cascade: a sequence shorter than the shared prefix sees only its own
+  // tokens of it; ctx_row is the lane row's key count
+  int ctx_row = kv_len;
+  if (casc && wq0 + (int)(threadIdx.x % 32) < rows_r) {
+    int c = p.context_lens[row_base + (wq0 + (int)(threadIdx.x % 32)) / p.group] - k0;
+    ctx_row = c < 0 ? 0 : (c < kv_len ? c : kv_len);
+  }
+  int ctx_min_w = ctx_row;
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) ctx_min_w = min(ctx_min_w, __shfl_xor(ctx_min_w, off));
+  const int keys_wg = casc ? kv_len : min(kv_len, P + tok_last_wg + 1);
   const int nst = (keys_wg + kStage - 1) / kStage;
-  const int keys_w = wave_active ? min(kv_len, P + tok_last_w + 1) : 0;
-  const int nsub = (keys_w + 31) / 32;                        // 32-key sub-tiles of this wave
-  const int full_keys_w = min(P + tok_first_w + 1, kv_len);  // keys below need no mask in this wave
-  if (nst == 0) return true;                                 // uniform over the work-group
+  const int keys_w = wave_active ? (casc ? kv_len : min(kv_len, P + tok_last_w + 1)) : 0;
+  const int nsub = (keys_w + 31) / 32;  // 32-key sub-tiles of this wave
+  // keys below need no mask in this wave
+  const int full_keys_w = casc ? __builtin_amdgcn_readfirstlane(ctx_min_w) : min(P + tok_first_w + 1, kv_len);
+  if (nst == 0) return true;  // uniform over the work-group
 
   // ---- Q^T fragments for this lane's row ----
   const int row = wq0 + c32;
@@ -341,7 +372,7 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     if (rvalid) v = load_frag8(qrow + 16 * c + 8 * h0);
     qf[c] = v;
   }
-  const int lim = P + tok;  // last key position this row may see
+  const int lim = casc ? ctx_row - 1 : P + tok;  // last key position this row may see
   const float c2 = p.qk_scale_log2;
 
   // LDS byte addresses of this lane's operands (buffer 0, sub-tile 0)
@@ -823,6 +854,20 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
   {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
     l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  if (casc) {  // unnormalised partial (O, m, l) of each (sequence, head) for the combine
+    if (rvalid) {
+      const int64_t srow = ((int64_t)split * p.total_rows + row_base + tok) * p.hq + qh;
+      float* orow = p.ws_o + srow * D;
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          *reinterpret_cast<f32x4*>(orow + 32 * n + 8 * k + 4 * h0) =
+              f32x4{acc[n][4 * k], acc[n][4 * k + 1], acc[n][4 * k + 2], acc[n][4 * k + 3]};
+      if (h0 == 0) *reinterpret_cast<f32x2*>(p.ws_ml + srow * 2) = f32x2{m_run, l_run};
+    }
+    return true;
   }
   if (rvalid) {
     const float inv = p.v_scale / l_run;

@@ -1,0 +1,86 @@
+"""Cascade decode (pkv_cascade_decode_attn) against the oracle: grouped
+shared-prefix batches across dtypes, block sizes and head dims, members
+shorter than their group's prefix, empty sequences, groups without a shared
+prefix, an fp8 cache, and the full 256-sequence shared-prompt workload."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import prefix_reuse_amd as pkv
+import workloads
+from _helpers import (TOL, fp8_inputs_from_pools, gpu_decode, nan_fp8_caches, np64, oracle_decode,
+                      oracle_fp8_caches, report)
+
+pytestmark = pytest.mark.gpu
+
+GROUPS = [
+    [([40, 70, 33, 200], 32)],
+    [([40, 70, 33], 32), ([5], 0), ([100, 90, 300], 64), ([17], 16)],
+    [([20, 50], 48), ([0, 17], 16), ([16, 33], 16), ([1], 0)],
+    [([500, 700, 640, 900, 513], 496)],
+]
+
+
+def run_cascade(case, device="cuda", k_scale=1.0, v_scale=1.0, caches=None):
+    if caches is None:
+        kc, vc = pkv.caches_from_logical(case.k_pool, case.v_pool, device)
+        pkv.append(case.k_new.to(device), case.v_new.to(device), case.slot_mapping.to(device), kc, vc)
+    else:
+        kc, vc = caches
+    out = pkv.cascade_decode_attn(case.q.to(device), kc, vc, case.block_tables.to(device),
+                                  case.context_lens.to(device), case.meta["group_starts"].to(device),
+                                  case.meta["shared_lens"].to(device), case.scale, k_scale=k_scale,
+                                  v_scale=v_scale)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("gi", range(len(GROUPS)))
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("d,b,hq,hkv", [(128, 16, 32, 8), (128, 32, 8, 2), (64, 16, 6, 2), (64, 32, 16, 1)])
+def test_cascade_matches_oracle(gi, dtype, d, b, hq, hkv):
+    groups = [(lens, (shared // b) * b) for lens, shared in GROUPS[gi]]
+    case = workloads.make_grouped_decode_case(500 + gi, groups, hq, hkv, d, b, dtype)
+    print(f"groups {gi} {dtype} d={d} B={b} {hq}/{hkv}", flush=True)
+    got = np64(run_cascade(case))
+    ref = oracle_decode(case)
+    assert report(f"cascade g{gi}", got, ref, dtype, TOL[dtype]) <= 1.0
+
+
+@pytest.mark.parametrize("q_dtype", [torch.bfloat16, torch.float16])
+def test_cascade_fp8_cache(q_dtype):
+    case = workloads.make_grouped_decode_case(610, [([300, 130, 257], 128), ([64], 0), ([90, 45], 32)], 8, 2, 128,
+                                              32, torch.float32)
+    case.q = case.q.to(q_dtype)
+    inp = fp8_inputs_from_pools(case)
+    kc, vc = nan_fp8_caches(case)
+    pkv.append(inp.rows_k.cuda(), inp.rows_v.cuda(), inp.slots.cuda(), kc, vc, inp.k_scale, inp.v_scale)
+    got = np64(run_cascade(case, k_scale=inp.k_scale, v_scale=inp.v_scale, caches=(kc, vc)))
+    ek, ev = oracle_fp8_caches(case, inp)
+    ref = oracle.decode_attention(np64(case.q), ek, ev, case.block_tables.numpy(), case.context_lens.numpy(),
+                                  case.scale, fp8=True, k_scale=inp.k_scale, v_scale=inp.v_scale)
+    assert report("cascade fp8", got, ref, q_dtype, TOL["fp8"]) <= 1.0
+
+
+def test_cascade_workload_shared_prompt_full():
+    """256 sequences on one 1,000-token system prompt (31 shared 32-token
+    blocks): every output against the oracle, and close to the plain decode."""
+    case = workloads.config3_shared_prefix_decode()
+    case.meta["group_starts"] = torch.tensor([0, case.num_seqs], dtype=torch.int32)
+    case.meta["shared_lens"] = torch.full((case.num_seqs,), case.shared_blocks * case.block_size, dtype=torch.int32)
+    got = run_cascade(case)
+    ref = oracle_decode(case)
+    assert report("cascade config3", np64(got), ref, torch.bfloat16, TOL[torch.bfloat16]) <= 1.0
+    plain = gpu_decode(case).out
+    assert report("cascade vs decode", np64(got), np64(plain)) <= 2 * TOL[torch.bfloat16] + 8e-3
+
+
+def test_cascade_is_deterministic_and_ignores_physical_order():
+    groups = [([300, 257, 140], 128), ([33], 0)]
+    case = workloads.make_grouped_decode_case(620, groups, 16, 4, 128, 16, torch.bfloat16)
+    a = run_cascade(case)
+    b = run_cascade(case)
+    assert torch.equal(a, b)

@@ -135,7 +135,7 @@ def _layout_sequences(g, lens, block_size, extra_free_blocks=0, shared=None):
     nseq = len(lens)
     nblk_seq = [(n + block_size - 1) // block_size for n in lens]
     n_shared = 0 if shared is None else shared
-    private = [nb - n_shared for nb in nblk_seq]
+    private = [max(nb - n_shared, 0) for nb in nblk_seq]  # a member may end inside the shared blocks
     used = n_shared + sum(private)
     pool = used + extra_free_blocks
     perm = torch.randperm(pool, generator=g)
@@ -205,12 +205,17 @@ def make_decode_case(seed: int, lens: List[int], num_q_heads: int, num_kv_heads:
                 v_pool[blk, off] = v_tail[t - n_shared * block_size]
     k_new = _randn(g, (nseq, num_kv_heads, head_dim), dtype)
     v_new = _randn(g, (nseq, num_kv_heads, head_dim), dtype)
-    # poison everything that is not a live, already-cached token
-    pre_lens = [max(n - 1, 0) for n in lens]
+    # poison everything that is not a live, already-cached token; the shared
+    # blocks hold the whole shared prefix, and a sequence that ends inside
+    # them has its newest token there already (nothing to append)
+    in_shared = [0 < n <= n_shared * block_size for n in lens]
+    pre_lens = [n if sh else max(n - 1, 0) for n, sh in zip(lens, in_shared)]
     live = _live_mask(bt, pre_lens, nb, block_size)
+    if n_shared:
+        live[bt[0, :n_shared].long()] = True
     k_pool[~live] = _poison_value(dtype)
     v_pool[~live] = _poison_value(dtype)
-    slots = torch.tensor([_slot(bt[s], lens[s] - 1, block_size) if lens[s] > 0 else -1
+    slots = torch.tensor([_slot(bt[s], lens[s] - 1, block_size) if lens[s] > 0 and not in_shared[s] else -1
                           for s in range(nseq)], dtype=torch.int64)
     return DecodeCase(
         name=name, dtype=dtype, block_size=block_size, num_q_heads=num_q_heads,
