@@ -168,6 +168,31 @@ def run_decode_call(pkv, t):
     pkv.decode_attn(t["q"], t["kc"], t["vc"], t["bt"], t["cl"], c.scale, out=t["out"], workspace=t["ws"])
 
 
+def shared_prefix_setup(torch, pkv, workloads, dev):
+    """256 sequences on one 1,000-token system prompt (31 aliased 32-token
+    blocks), bf16: one group for the cascade decode."""
+    case = workloads.config3_shared_prefix_decode()
+    kc, vc = pkv.caches_from_logical(case.k_pool, case.v_pool, dev)
+    pkv.append(case.k_new.to(dev), case.v_new.to(dev), case.slot_mapping.to(dev), kc, vc)
+    t = {"case": case, "kc": kc, "vc": vc, "q": case.q.to(dev), "bt": case.block_tables.to(dev),
+         "cl": case.context_lens.to(dev),
+         "gs": torch.tensor([0, case.num_seqs], dtype=torch.int32, device=dev),
+         "sl": torch.full((case.num_seqs,), case.shared_blocks * case.block_size, dtype=torch.int32, device=dev)}
+    t["out"] = torch.empty_like(t["q"])
+    need = max(pkv.cascade_workspace_bytes(case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim),
+               pkv.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                                          case.block_tables.shape[1], case.block_size))
+    t["ws"] = torch.zeros(need, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    return t
+
+
+def run_cascade_call(pkv, t):
+    c = t["case"]
+    pkv.cascade_decode_attn(t["q"], t["kc"], t["vc"], t["bt"], t["cl"], t["gs"], t["sl"], c.scale, out=t["out"],
+                            workspace=t["ws"])
+
+
 def run_prefill_call(pkv, t):
     c = t["case"]
     pkv.suffix_prefill_attn(t["q"], t["kc"], t["vc"], t["bt"], t["pl"], t["sl"], c.scale, out=t["out"])
@@ -297,7 +322,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-long-context", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "long"], default=None,
+    ap.add_argument("--no-shared-prefix", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill", "long", "shared"], default=None,
                     help="run only this kernel's launches (for profiler runs)")
     ap.add_argument("--ingest-profile", nargs=5, metavar=("NAME", "TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "KERNEL_REGEX"),
                     help="summarise rocprofv3 csv output into profiles/ (no GPU needed)")
@@ -322,9 +348,11 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     if args.only is not None:
-        setup = {"decode": decode_setup, "prefill": prefill_setup, "long": long_context_setup}[args.only]
+        setup = {"decode": decode_setup, "prefill": prefill_setup, "long": long_context_setup,
+                 "shared": shared_prefix_setup}[args.only]
         call = {"decode": run_decode_call, "prefill": run_prefill_call,
-                "long": lambda pkv, t: run_long_context_decode(pkv, t, t["layers"][0])}[args.only]
+                "long": lambda pkv, t: run_long_context_decode(pkv, t, t["layers"][0]),
+                "shared": run_cascade_call}[args.only]
         t = setup(torch, pkv, workloads, dev) if args.only != "long" else setup(torch, pkv, workloads, dev, 1)
         for _ in range(args.warmup):
             call(pkv, t)
@@ -415,6 +443,38 @@ def main() -> int:
                          "avg_launch_us": round(pre_ms * 1e3, 2)},
             "suffix_tokens_per_s": round(int(pc.suffix_lens.sum()) / (pre_ms * 1e-3), 1),
         }
+
+    # ---------------- shared-prefix decode: cascade vs plain ----------------
+    if not args.no_shared_prefix:
+        torch.cuda.empty_cache()
+        sp = shared_prefix_setup(torch, pkv, workloads, dev)
+        sc = sp["case"]
+        casc = lambda: run_cascade_call(pkv, sp)
+        plain = lambda: run_decode_call(pkv, sp)
+        for _ in range(args.warmup):
+            casc()
+            plain()
+        warm_clocks(torch, casc, 0.3)
+        c_ms = time_launches(torch, stream, casc, args.steps)
+        p_ms = time_launches(torch, stream, plain, args.steps)
+        ub, lb = sc.unique_kv_read_bytes(), sc.kv_read_bytes()
+        straffic = load_traffic("cascade_shared_prefix_256x1000_bf16", KERNEL_SOURCES)
+        result["shared_prefix_decode"] = {
+            "metric": "shared-prefix decode KV-read GB/s (unique bytes)", "value": round(ub / (c_ms * 1e-3) / 1e9, 1),
+            "unit": "GB/s",
+            "config": {"workload": "256 sequences sharing a 1,000-token system prompt (31 aliased 32-token blocks) "
+                                   "+ 50..500 private tokens, 32/8 heads, d=128, bf16, B=32",
+                       "unique_kv_bytes": ub, "logical_kv_bytes": lb},
+            "cascade_us": round(c_ms * 1e3, 2), "plain_decode_us": round(p_ms * 1e3, 2),
+            "plain_decode_unique_gbs": round(ub / (p_ms * 1e-3) / 1e9, 1),
+            "roofline": {"kernel": "pkv_cascade_decode_attn (shared part + decode_kernel + combine)", "bound": "hbm",
+                         "achieved": round(ub / (c_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(ub / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": None if straffic is None else straffic["bytes_per_launch"],
+                         "avg_launch_us": round(c_ms * 1e3, 2), "algorithmic_bytes_per_launch": ub},
+        }
+        del sp
+        torch.cuda.empty_cache()
 
     # ---------------- long-context fp8 decode: 32 layers per step ----------------
     if not args.no_long_context:
