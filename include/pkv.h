@@ -193,9 +193,10 @@ int pkv_suffix_prefill_attn(const pkv_tensor* q_suffix, const pkv_tensor* k_cach
  * needs on the CURRENT device: the decode workspace (rounded up to 16 bytes)
  * plus, for the shared part, one partial result per (key chunk, sequence,
  * query head): splits * num_seqs * H_q * (head_dim + 2) floats, where the
- * shared keys are cut into splits = min(16, max(1, CUs / row tiles)) chunks so
- * that the shared part fills the device (row tiles = H_kv * ceil(num_seqs * G
- * / 256)). Returns 0 on invalid sizes.
+ * shared keys are cut into splits = min(4, max(1, CUs / row tiles)) chunks so
+ * that the shared part fills more of the device (row tiles = H_kv *
+ * ceil(num_seqs * G / 256)); the environment variable PKV_CASCADE_SPLITS
+ * (1..16) replaces that count for both calls. Returns 0 on invalid sizes.
  */
 size_t pkv_cascade_workspace_bytes(int64_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                    int32_t head_dim);

@@ -161,8 +161,10 @@ size_t decode_ws_bytes(int64_t num_seqs, int32_t hq, int32_t hkv, int32_t d, pkv
 }
 
 // cascade: how many work-groups share one row tile of the shared part, so
-// that the shared part fills the device (at most 16: the combine's limit)
-// PKV_CASCADE_SPLITS (1..16) forces the count.
+// that the shared part fills more of the device; at most 4, because every
+// split adds a partial per (sequence, head) that is written and read back
+// (measured on 256 sequences x 32 heads: 1 split 113 us, 2: 103, 4: 103,
+// 8: 106, 16: 123). PKV_CASCADE_SPLITS (1..16) forces the count.
 int cascade_splits(int64_t num_seqs, int32_t hq, int32_t hkv) {
   if (const char* env = getenv("PKV_CASCADE_SPLITS")) {
     const long forced = atol(env);
@@ -171,7 +173,7 @@ int cascade_splits(int64_t num_seqs, int32_t hq, int32_t hkv) {
   constexpr int64_t W = pkv::kPrefillRowsPerWg;
   const int64_t tiles = (int64_t)hkv * ((num_seqs * (hq / hkv) + W - 1) / W);
   int64_t sp = device_cus() / (tiles > 0 ? tiles : 1);
-  return (int)(sp < 1 ? 1 : (sp > 16 ? 16 : sp));
+  return (int)(sp < 1 ? 1 : (sp > 4 ? 4 : sp));
 }
 
 // cascade: the decode workspace (rounded up to 16 bytes), then the shared

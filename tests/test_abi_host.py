@@ -165,3 +165,29 @@ def test_empty_batches_are_accepted_without_launch():
     assert decode(T([0, 4, 64], F16), kc, vc, T([0, 4], I32), T([0], I32), T([0, 4, 64], F16)) == 0
     f = pkv.lib.pkv_append
     assert f(R(T([0, 2, 64], F16)), R(T([0, 2, 64], F16)), R(T([0], I64)), R(kc), R(vc), 1.0, 1.0, None) == 0
+
+
+def cascade(q, kc, vc, bt, cl, gs, sl, out, ws=None, ws_bytes=0):
+    return pkv.lib.pkv_cascade_decode_attn(R(q), R(kc), R(vc), R(bt), R(cl), R(gs), R(sl), 0.125, 1.0, 1.0,
+                                           ws, ws_bytes, R(out), None)
+
+
+def test_cascade_rejects_bad_arguments():
+    kc, vc = caches()
+    q, out = T([3, 4, 64], F16), T([3, 4, 64], F16)
+    bt, cl, gs, sl = T([3, 8], I32), T([3], I32), T([2], I32), T([3], I32)
+    assert cascade(T([3, 4, 64], F32), *caches(dt=F32), bt, cl, gs, sl, T([3, 4, 64], F32)) == 2  # matrix cores
+    assert cascade(q, kc, vc, bt, cl, T([2], I64), sl, out) == 2
+    assert cascade(q, kc, vc, bt, cl, gs, T([2], I32), out) == 3          # one shared length per sequence
+    assert cascade(q, kc, vc, bt, cl, T([0], I32), sl, out) == 3          # group_starts needs an entry
+    need = pkv.cascade_workspace_bytes(3, 4, 2, 64)
+    assert need > pkv.decode_workspace_bytes(3, 4, 2, 64, 8, 16)
+    rc = cascade(q, kc, vc, bt, cl, gs, sl, out, ws=FAKE, ws_bytes=need - 1)
+    assert rc == 6 and "cascade workspace" in err()
+
+
+def test_cascade_workspace_size_formula(monkeypatch):
+    monkeypatch.setenv("PKV_DECODE_WAVES", "64")
+    monkeypatch.setenv("PKV_CASCADE_SPLITS", "3")
+    dec = pkv.decode_workspace_bytes(5, 32, 8, 128, 100, 32)
+    assert pkv.cascade_workspace_bytes(5, 32, 8, 128) == (dec + 15) // 16 * 16 + 3 * 5 * 32 * 130 * 4
