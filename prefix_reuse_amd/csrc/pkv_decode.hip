@@ -409,10 +409,11 @@ __global__ __launch_bounds__(64, 3) void decode_kernel(DecodeParams p) {
 }
 
 // Merge the partials of the sequences that several waves shared, in wave
-// order. One work-group per (sequence, group of 8 query heads); each thread
-// owns 4 consecutive dims of one head. Sequences that one wave covered
-// entirely already hold their output; empty sequences get zero rows here.
-constexpr int kCombineHeads = 8;
+// order. One work-group per (sequence, pair of query heads), so that even a
+// handful of long sequences spreads over many work-groups; each thread owns 4
+// consecutive dims of one head. Sequences that one wave covered entirely
+// already hold their output; empty sequences get zero rows here.
+constexpr int kCombineHeads = 2;
 
 template <typename TQ, int D, int BLK>
 __global__ __launch_bounds__(kCombineHeads * D / 4) void decode_combine_kernel(DecodeParams p) {
@@ -478,7 +479,6 @@ __global__ __launch_bounds__(kCombineHeads * D / 4) void decode_combine_kernel(D
   }
 #pragma unroll
   for (int i = 0; i < kFew; ++i) M = fmaxf(M, ml[i][0]);
-  for (int i = kFew; i < n; ++i) M = fmaxf(M, p.ws_ml[(row0 + (int64_t)i * p.hq) * 2]);
 #pragma unroll
   for (int i = 0; i < kMaxSplits; ++i) {
     const float f = i < nsh ? exp2f(sml[i][0] - M) : 0.f;
@@ -491,11 +491,29 @@ __global__ __launch_bounds__(kCombineHeads * D / 4) void decode_combine_kernel(D
     L += ml[i][1] * f;
     O += o[i] * f;
   }
-  for (int i = kFew; i < n; ++i) {
-    const int64_t row = row0 + (int64_t)i * p.hq;
-    const float f = exp2f(p.ws_ml[row * 2] - M);
-    L += p.ws_ml[row * 2 + 1] * f;
-    O += *reinterpret_cast<const f32x4*>(p.ws_o + row * D + d0) * f;
+  // further partials (long contexts spread over many waves) in batches of
+  // kFew, each loaded in one round and merged under a running maximum
+  for (int i0 = kFew; i0 < n; i0 += kFew) {
+#pragma unroll
+    for (int i = 0; i < kFew; ++i) {
+      const int64_t row = row0 + (int64_t)(i0 + i) * p.hq;
+      const bool ok = i0 + i < n;
+      ml[i] = ok ? *reinterpret_cast<const f32x2*>(p.ws_ml + row * 2) : f32x2{-INFINITY, 0.f};
+      o[i] = ok ? *reinterpret_cast<const f32x4*>(p.ws_o + row * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < kFew; ++i) Mb = fmaxf(Mb, ml[i][0]);
+    const float r = exp2f(M - Mb);  // M is finite: the first round held a partial
+    L *= r;
+    O *= r;
+    M = Mb;
+#pragma unroll
+    for (int i = 0; i < kFew; ++i) {
+      const float f = i0 + i < n ? exp2f(ml[i][0] - M) : 0.f;
+      L += ml[i][1] * f;
+      O += o[i] * f;
+    }
   }
   const float inv = p.v_scale / L;
   TQx4 v;
