@@ -272,7 +272,7 @@ constexpr int kLdsBytes = kRing * 2 * kStage * D * 2;
 
 // The rows of one work-group. Returns false (having written nothing) when a
 // kFast pass met a value it cannot convert; the caller then runs the exact pass.
-template <typename TQ, typename TC, int D, int BLK, bool kFast>
+template <typename TQ, typename TC, int D, int BLK, bool kFast, bool kCasc>
 __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg) {
   typedef Types<TQ, TC, kFast> T;
   typedef typename T::VOp VOp;
@@ -292,7 +292,7 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
   int tile = logical % p.tiles_per_head;
   // cascade decode's shared part: the requests are groups of sequences, and
   // key_splits work-groups share a row tile, each on one chunk of the keys
-  const bool casc = p.group_starts != nullptr;
+  constexpr bool casc = kCasc;  // a kernel of its own: the suffix prefill carries none of it
   int split = 0;
   if (casc) {
     split = tile % p.key_splits;
@@ -887,20 +887,21 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
   return true;
 }
 
-template <typename TQ, typename TC, int D, int BLK>
+// kCasc: the shared part of a cascade decode (PrefillParams::group_starts)
+template <typename TQ, typename TC, int D, int BLK, bool kCasc>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes<D>];
   int wg = blockIdx.x;
   if constexpr (std::is_same<TC, bf16_t>::value) {
-    if (!attend<TQ, TC, D, BLK, true>(p, lds, wg)) {
+    if (!attend<TQ, TC, D, BLK, true, kCasc>(p, lds, wg)) {
       // rare: redo exactly. The empty asm hides that this pass works on the
       // same work-group, so nothing computed for the fast pass is kept alive
       // for it.
       asm volatile("" : "+s"(wg));
-      attend<TQ, TC, D, BLK, false>(p, lds, wg);
+      attend<TQ, TC, D, BLK, false, kCasc>(p, lds, wg);
     }
   } else {
-    attend<TQ, TC, D, BLK, false>(p, lds, wg);
+    attend<TQ, TC, D, BLK, false, kCasc>(p, lds, wg);
   }
 }
 
@@ -908,7 +909,10 @@ template <typename TQ, typename TC, int D, int BLK>
 hipError_t launch_typed(const PrefillParams& p, hipStream_t stream) {
   const int64_t wgs = (int64_t)p.hkv * p.tiles_per_head;
   if (wgs == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_kernel<TQ, TC, D, BLK>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, p);
+  if (p.group_starts)
+    hipLaunchKernelGGL((prefill_kernel<TQ, TC, D, BLK, true>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((prefill_kernel<TQ, TC, D, BLK, false>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
