@@ -113,6 +113,37 @@ def prefill_setup(torch, pkv, workloads, dev):
     return t
 
 
+def prefill_fp8_setup(torch, pkv, workloads, dev):
+    """The same suffix-prefill workload over an fp8 e4m3fn cache: every cached
+    row and every suffix row is quantized through pkv_append (scale = amax/448
+    for K and for V); q and the output stay bf16."""
+    import numpy as np
+
+    case = workloads.config4_suffix_prefill()
+    nb, b, h, d = case.k_pool.shape
+    kc, vc = pkv.empty_caches(nb, b, h, d, torch.float8_e4m3fn, dev)
+    kc.view(torch.uint8).fill_(workloads.fp8_nan_code)
+    vc.view(torch.uint8).fill_(workloads.fp8_nan_code)
+    live = (~torch.isnan(case.k_pool[:, :, 0, 0].float())).nonzero()
+    slots = torch.cat([live[:, 0] * b + live[:, 1], case.slot_mapping]).to(dev)
+    rows = {w: torch.cat([pool[live[:, 0], live[:, 1]], new]).to(dev)
+            for w, pool, new in (("k", case.k_pool, case.k_new), ("v", case.v_pool, case.v_new))}
+    sc = {w: float(np.float32(rows[w].float().abs().max().item()) / np.float32(448.0)) for w in rows}
+    pkv.append(rows["k"], rows["v"], slots, kc, vc, sc["k"], sc["v"])
+    t = {"case": case, "kc": kc, "vc": vc, "q": case.q_suffix.to(dev), "bt": case.block_tables.to(dev),
+         "pl": case.prefix_lens.to(dev), "sl": case.suffix_lens.to(dev), "ks": sc["k"], "vs": sc["v"]}
+    t["out"] = torch.empty_like(t["q"])
+    del rows
+    torch.cuda.synchronize()
+    return t
+
+
+def run_prefill_fp8_call(pkv, t):
+    c = t["case"]
+    pkv.suffix_prefill_attn(t["q"], t["kc"], t["vc"], t["bt"], t["pl"], t["sl"], c.scale, out=t["out"],
+                            k_scale=t["ks"], v_scale=t["vs"])
+
+
 def long_context_setup(torch, pkv, workloads, dev, num_layers=32):
     """Per-layer fp8 caches of the long-context workload, every token quantized
     through pkv_append from N(0,1) rows drawn on the device (scale = amax/448
@@ -323,7 +354,7 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-long-context", action="store_true")
     ap.add_argument("--no-shared-prefix", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "long", "shared"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "prefill_fp8", "long", "shared"], default=None,
                     help="run only this kernel's launches (for profiler runs)")
     ap.add_argument("--ingest-profile", nargs=5, metavar=("NAME", "TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "KERNEL_REGEX"),
                     help="summarise rocprofv3 csv output into profiles/ (no GPU needed)")
@@ -348,9 +379,9 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     if args.only is not None:
-        setup = {"decode": decode_setup, "prefill": prefill_setup, "long": long_context_setup,
-                 "shared": shared_prefix_setup}[args.only]
-        call = {"decode": run_decode_call, "prefill": run_prefill_call,
+        setup = {"decode": decode_setup, "prefill": prefill_setup, "prefill_fp8": prefill_fp8_setup,
+                 "long": long_context_setup, "shared": shared_prefix_setup}[args.only]
+        call = {"decode": run_decode_call, "prefill": run_prefill_call, "prefill_fp8": run_prefill_fp8_call,
                 "long": lambda pkv, t: run_long_context_decode(pkv, t, t["layers"][0]),
                 "shared": run_cascade_call}[args.only]
         t = setup(torch, pkv, workloads, dev) if args.only != "long" else setup(torch, pkv, workloads, dev, 1)
@@ -443,6 +474,28 @@ def main() -> int:
                          "avg_launch_us": round(pre_ms * 1e3, 2)},
             "suffix_tokens_per_s": round(int(pc.suffix_lens.sum()) / (pre_ms * 1e-3), 1),
         }
+        del p
+        torch.cuda.empty_cache()
+        # the same prefill over an fp8 e4m3fn cache (multi-turn with an fp8 KV cache)
+        p8 = prefill_fp8_setup(torch, pkv, workloads, dev)
+        for _ in range(args.warmup):
+            run_prefill_fp8_call(pkv, p8)
+        warm_clocks(torch, lambda: run_prefill_fp8_call(pkv, p8))
+        f8_ms = time_launches(torch, stream, lambda: run_prefill_fp8_call(pkv, p8), args.steps)
+        f8_tflops = flops / (f8_ms * 1e-3) / 1e12
+        f8traffic = load_traffic("prefill_16x1900p100_fp8", KERNEL_SOURCES)
+        result["suffix_prefill_fp8_kv"] = {
+            "metric": "suffix-prefill TFLOP/s, fp8 KV cache", "value": round(f8_tflops, 2), "unit": "TFLOP/s",
+            "config": {"workload": "16 requests x (1,900 cached + 100 new tokens), 32/8 heads, d=128, fp8 e4m3fn "
+                                   "K/V (per-tensor scales), bf16 q/out, B=16", "flop_per_launch": flops},
+            "roofline": {"kernel": "prefill_kernel (fp8 cache)", "bound": "mfma", "achieved": round(f8_tflops, 2),
+                         "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(f8_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                         "traffic": None if f8traffic is None else f8traffic["bytes_per_launch"],
+                         "avg_launch_us": round(f8_ms * 1e3, 2)},
+        }
+        del p8
+        torch.cuda.empty_cache()
 
     # ---------------- shared-prefix decode: cascade vs plain ----------------
     if not args.no_shared_prefix:
@@ -478,8 +531,6 @@ def main() -> int:
 
     # ---------------- long-context fp8 decode: 32 layers per step ----------------
     if not args.no_long_context:
-        if not args.no_prefill:
-            del p
         torch.cuda.empty_cache()
         lt = long_context_setup(torch, pkv, workloads, dev)
         lc = lt["case"]

@@ -86,10 +86,10 @@ class PrefixCache:
         self._h = h
         self.block_size = block_size
 
-    def __del__(self):
+    def __del__(self, _destroy=lib.pkv_pc_destroy):  # bound now: module globals may be gone at exit
         h = getattr(self, "_h", None)
         if h is not None and h.value:
-            lib.pkv_pc_destroy(h)
+            _destroy(h)
             self._h = None
 
     def admit(self, tokens: Sequence[int], salt: int = 0, extra: int = 0
@@ -146,10 +146,10 @@ class RadixTree:
         self._h = h
         self.page = page
 
-    def __del__(self):
+    def __del__(self, _destroy=lib.pkv_radix_destroy):
         h = getattr(self, "_h", None)
         if h is not None and h.value:
-            lib.pkv_radix_destroy(h)
+            _destroy(h)
             self._h = None
 
     def match_prefix(self, tokens: Sequence[int]) -> Tuple[int, List[int]]:
