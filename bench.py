@@ -36,8 +36,10 @@ sys.path.insert(0, str(ROOT))
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak
-KERNEL_SOURCES = ["prefix_reuse_amd/csrc/pkv_decode.hip", "prefix_reuse_amd/csrc/pkv_prefill.hip",
-                  "prefix_reuse_amd/csrc/pkv_device.hpp", "prefix_reuse_amd/csrc/pkv_append.hip"]
+# the device code and the launch planning behind every profiled kernel
+KERNEL_SOURCES = [f"prefix_reuse_amd/csrc/{f}" for f in (
+    "pkv_decode.hip", "pkv_decode_body.hpp", "pkv_prefill.hip", "pkv_prefill_body.hpp", "pkv_cascade.hip",
+    "pkv_device.hpp", "pkv_internal.hpp", "pkv_append.hip", "pkv_api.hip")]
 
 
 def sources_hash(files) -> str:

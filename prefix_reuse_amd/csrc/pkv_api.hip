@@ -160,24 +160,23 @@ size_t decode_ws_bytes(int64_t num_seqs, int32_t hq, int32_t hkv, int32_t d, pkv
   return slots * hq * (size_t)(d + 2) * sizeof(float) + (size_t)num_seqs * 2 * sizeof(int32_t);
 }
 
-// cascade: how many work-groups share one row tile of the shared part, so
-// that the shared part fills more of the device; at most 4, because every
-// split adds a partial per (sequence, head) that is written and read back
-// (measured on 256 sequences x 32 heads: 1 split 113 us, 2: 103, 4: 103,
-// 8: 106, 16: 123). PKV_CASCADE_SPLITS (1..16) forces the count.
+// cascade: how many work-groups share one row tile of the shared part (each
+// takes one chunk of the shared keys). The shared part runs beside the
+// private-token decode in one launch, so it needs only to finish before the
+// decode does, and every split adds a partial per (sequence, head) that is
+// written and read back. PKV_CASCADE_SPLITS (1..16) forces the count.
 int cascade_splits(int64_t num_seqs, int32_t hq, int32_t hkv) {
   if (const char* env = getenv("PKV_CASCADE_SPLITS")) {
     const long forced = atol(env);
     if (forced >= 1 && forced <= 16) return (int)forced;
   }
-  constexpr int64_t W = pkv::kPrefillRowsPerWg;
-  const int64_t tiles = (int64_t)hkv * ((num_seqs * (hq / hkv) + W - 1) / W);
-  int64_t sp = device_cus() / (tiles > 0 ? tiles : 1);
-  return (int)(sp < 1 ? 1 : (sp > 4 ? 4 : sp));
+  (void)num_seqs, (void)hq, (void)hkv;
+  return 1;
 }
 
-// cascade: the decode workspace (rounded up to 16 bytes), then the shared
-// partials O [splits, S, Hq, d] and (m, l) [splits, S, Hq, 2]
+// cascade: the decode workspace (rounded up to 16 bytes; sized for a decode on
+// every CU, the most the launch uses), then the shared partials
+// O [splits, S, Hq, d] and (m, l) [splits, S, Hq, 2]
 size_t cascade_ws_bytes(int64_t num_seqs, int32_t hq, int32_t hkv, int32_t d, pkv::DecodePlan* plan_out,
                         size_t* shared_offset, int* splits_out) {
   const size_t dec = (decode_ws_bytes(num_seqs, hq, hkv, d, plan_out) + 15) / 16 * 16;
@@ -261,9 +260,11 @@ int pkv_cascade_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, cons
   float* sh_ml = sh_o + (size_t)splits * S * hq * cg.dim;
   const float qk = scale * (fp8 ? k_scale : 1.0f) * pkv::kLog2eHost;
 
-  // 1. every group's queries over its shared prefix, once (matrix cores)
+  // the shared part: every group's queries over its shared prefix, once per
+  // row tile (matrix cores)
+  pkv::PrefillParams sp{};
+  int64_t shared_wgs = 0;
   if (G > 0) {
-    pkv::PrefillParams sp{};
     sp.q = q->data; sp.q_s0 = q->stride[0]; sp.q_s1 = q->stride[1];
     sp.k_cache = k_cache->data; sp.v_cache = v_cache->data;
     sp.block_tables = reinterpret_cast<const int32_t*>(block_tables->data);
@@ -271,8 +272,10 @@ int pkv_cascade_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, cons
     sp.num_reqs = (int32_t)G; sp.hq = (int32_t)hq; sp.hkv = cg.hkv; sp.group = (int32_t)(hq / cg.hkv);
     sp.num_blocks = (int32_t)cg.num_blocks; sp.total_rows = S;
     constexpr int64_t W = pkv::kPrefillRowsPerWg;
+    // an upper bound on the row tiles (each group's last one may be partial);
+    // work-groups past a group list's real tiles return at once
     const int64_t tiles = ((S * sp.group + W - 1) / W + G) * splits;
-    if (tiles * cg.hkv > INT32_MAX) return fail(PKV_ERR_SHAPE, "problem too large for one launch");
+    if (tiles * cg.hkv > INT32_MAX / 2) return fail(PKV_ERR_SHAPE, "problem too large for one launch");
     sp.tiles_per_head = (int32_t)tiles;
     sp.key_splits = splits;
     sp.qk_scale_log2 = qk;
@@ -282,10 +285,16 @@ int pkv_cascade_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, cons
     sp.shared_lens = reinterpret_cast<const int32_t*>(shared_lens->data);
     sp.ws_o = sh_o;
     sp.ws_ml = sh_ml;
-    hipError_t e = pkv::launch_prefill(sp, to_dt(q->dtype), to_dt(cg.dtype), cg.dim, cg.block, (hipStream_t)stream);
-    if (e != hipSuccess) return fail(PKV_ERR_HIP, "cascade shared-prefix launch failed: %s", hipGetErrorString(e));
+    shared_wgs = (tiles * cg.hkv + 7) / 8 * 8;
   }
-  // 2. each sequence's own tokens, then the merge with its shared partial
+  // the private-token decode, on the compute units the shared part leaves
+  // (each shared work-group holds a whole CU), then the merge of all partials
+  const int cus = device_cus();
+  const int64_t busy = shared_wgs < cus / 2 ? shared_wgs : cus / 2;
+  const int32_t head_chunks = (int32_t)((hq / cg.hkv + 15) / 16);
+  const pkv::DecodePlan dplan = pkv::plan_decode(S, cg.hkv, head_chunks, (int32_t)(cus - busy));
+  if (dplan.waves_per_head > plan.waves_per_head)
+    return fail(PKV_ERR_WORKSPACE, "cascade decode plan exceeds its workspace");
   pkv::DecodeParams p{};
   p.q = q->data; p.q_s0 = q->stride[0]; p.q_s1 = q->stride[1];
   p.k_cache = k_cache->data; p.v_cache = v_cache->data;
@@ -294,10 +303,10 @@ int pkv_cascade_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, cons
   p.context_lens = reinterpret_cast<const int32_t*>(context_lens->data);
   p.out = out->data; p.o_s0 = out->stride[0]; p.o_s1 = out->stride[1];
   p.num_seqs = (int32_t)S; p.hq = (int32_t)hq; p.hkv = cg.hkv; p.group = (int32_t)(hq / cg.hkv);
-  p.head_chunks = (p.group + 15) / 16; p.num_blocks = (int32_t)cg.num_blocks;
-  p.waves_per_head = plan.waves_per_head;
-  p.total_wgs = plan.total_waves;
-  const size_t slots = (size_t)plan.waves_per_head + (size_t)S;
+  p.head_chunks = head_chunks; p.num_blocks = (int32_t)cg.num_blocks;
+  p.waves_per_head = dplan.waves_per_head;
+  p.total_wgs = dplan.total_waves;
+  const size_t slots = (size_t)dplan.waves_per_head + (size_t)S;
   p.ws_o = reinterpret_cast<float*>(workspace);
   p.ws_ml = p.ws_o + slots * hq * cg.dim;
   p.seq_info = reinterpret_cast<int32_t*>(p.ws_ml + slots * hq * 2);
@@ -307,7 +316,9 @@ int pkv_cascade_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, cons
   p.sh_o = sh_o;
   p.sh_ml = sh_ml;
   p.sh_splits = splits;
-  hipError_t e = pkv::launch_decode(p, to_dt(q->dtype), to_dt(cg.dtype), cg.dim, cg.block, (hipStream_t)stream);
+  if (shared_wgs + (p.total_wgs + 7) / 8 > INT32_MAX) return fail(PKV_ERR_SHAPE, "problem too large for one launch");
+  hipError_t e = pkv::launch_cascade(sp, p, (int)shared_wgs, to_dt(q->dtype), to_dt(cg.dtype), cg.dim, cg.block,
+                                     (hipStream_t)stream);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "cascade decode launch failed: %s", hipGetErrorString(e));
   return ok();
 }

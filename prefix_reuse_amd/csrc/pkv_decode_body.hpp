@@ -1,0 +1,381 @@
+// Device code of the paged decode (one wave per unit of the balanced
+// partition), shared by the decode kernel and the cascade kernel.
+#pragma once
+#include "pkv_device.hpp"
+#include "pkv_internal.hpp"
+
+#include <math.h>
+#include <type_traits>
+
+namespace pkv {
+namespace {
+
+constexpr int kChunk = 32;
+
+template <typename TQ, typename TC, int D>
+struct QFrag {
+  static constexpr bool kF32 = std::is_same<TC, float>::value;
+  static constexpr int kSteps = kF32 ? D / 4 : D / 32;
+  typedef typename std::conditional<kF32, float, typename Frag<TQ>::type>::type T;
+};
+
+// Load the B operand of the score product: Q^T for the lane's head.
+// 16-bit cache: step c covers dims 32c + 8g .. +8.
+// fp8 cache:    step c = 2u + h covers dims 64u + 16g + 8h .. +8 (matches the
+//               16-byte K loads, which carry 16 fp8 codes = two steps).
+// f32 cache:    step c = 4u + e covers dim 16u + 4g + e.
+template <typename TQ, typename TC, int D, typename QT>
+__device__ __forceinline__ void load_q(QT* qf, const TQ* qrow, bool valid, int g) {
+  constexpr int S = QFrag<TQ, TC, D>::kSteps;
+  if constexpr (std::is_same<TC, float>::value) {
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u) {
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (valid) v = *reinterpret_cast<const f32x4*>(qrow + 16 * u + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qf[4 * u + e] = v[e];
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < S; ++c) {
+      int d0 = std::is_same<TC, uint8_t>::value ? 64 * (c / 2) + 16 * g + 8 * (c % 2) : 32 * c + 8 * g;
+      typename Frag<TQ>::type v = {};
+      if (valid) v = load_frag8(qrow + d0);
+      qf[c] = v;
+    }
+  }
+}
+
+// Registers holding one 32-token chunk of K and V for one lane, as loaded.
+// K: the lane's A-operand rows of the two 16-token score tiles; piece c of a
+//    row covers dims c*4E + g*E .. +E, E = 16 / sizeof(TC) (16 bytes).
+// V: for each 16-dim output tile n, 8 consecutive tokens of V^T row 16n + c16.
+template <typename TC, int D>
+struct ChunkRegs {
+  static constexpr int E = 16 / sizeof(TC);
+  static constexpr int KN = D / (4 * E);
+  static constexpr int NT = D / 16;
+  static constexpr int VW = 8 * sizeof(TC) / 4;  // 32-bit words per V piece
+  u32x4 k[2][KN];
+  uint32_t v[NT][VW];
+};
+
+template <typename TC, int D, int BLK>
+__device__ __forceinline__ void load_chunk(ChunkRegs<TC, D>& r, const TC* kbase, const TC* vbase,
+                                           int blk0, int blk1, int hk, int hkv, int c16, int g) {
+  typedef ChunkRegs<TC, D> R;
+  const int64_t tile = (int64_t)BLK * D;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int tok = 8 * (c16 / 4) + 4 * a + (c16 % 4);  // chunk-relative token of this A row
+    const int blk = (BLK == 32 || tok < 16) ? blk0 : blk1;
+    const TC* krow = kbase + ((int64_t)blk * hkv + hk) * tile + (int64_t)(tok % BLK) * D + g * R::E;
+#pragma unroll
+    for (int c = 0; c < R::KN; ++c) r.k[a][c] = load_u32x4(krow + c * 4 * R::E);
+  }
+  const int tokv = 8 * g;
+  const int blkv = (BLK == 32 || tokv < 16) ? blk0 : blk1;
+  const TC* vt = vbase + ((int64_t)blkv * hkv + hk) * tile + (tokv % BLK) + (int64_t)c16 * BLK;
+#pragma unroll
+  for (int n = 0; n < R::NT; ++n) {
+    const TC* vr = vt + (int64_t)16 * n * BLK;
+    if constexpr (R::VW == 2) {
+      u32x2 w = load_u32x2(vr);
+      r.v[n][0] = w[0]; r.v[n][1] = w[1];
+    } else {
+#pragma unroll
+      for (int h = 0; h < R::VW / 4; ++h) {
+        u32x4 w = load_u32x4(vr + h * (16 / sizeof(TC)));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r.v[n][4 * h + e] = w[e];
+      }
+    }
+  }
+}
+
+// Scores of the 16-token tile a from loaded K rows: result element i is the
+// score of chunk token 8g + 4a + i for head c16.
+template <typename TQ, typename TC, int D, typename QT>
+__device__ __forceinline__ f32x4 score_tile(const ChunkRegs<TC, D>& r, int a, const QT* qf) {
+  typedef ChunkRegs<TC, D> R;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < R::KN; ++c) {
+    if constexpr (std::is_same<TC, float>::value) {
+      f32x4 kv = __builtin_bit_cast(f32x4, r.k[a][c]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = mfma16x16x4(kv[e], qf[4 * c + e], s);
+    } else if constexpr (std::is_same<TC, uint8_t>::value) {
+      u32x2 lo = {r.k[a][c][0], r.k[a][c][1]}, hi = {r.k[a][c][2], r.k[a][c][3]};
+      s = mfma16x16x32(fp8x8_to<TQ>(lo), qf[2 * c], s);
+      s = mfma16x16x32(fp8x8_to<TQ>(hi), qf[2 * c + 1], s);
+    } else {
+      s = mfma16x16x32(__builtin_bit_cast(typename Frag<TQ>::type, r.k[a][c]), qf[c], s);
+    }
+  }
+  return s;
+}
+
+// Chunk bookkeeping of the balanced partition: every 32-token chunk of every
+// sequence, in sequence order, is one unit of work; wave w of a KV head takes
+// units [w * per_wave, (w + 1) * per_wave).
+struct Partition {
+  int total;     // chunks of all sequences
+  int per_wave;  // ceil(total / waves per head)
+};
+
+__device__ __forceinline__ int ctx_of(const DecodeParams& p, int s, int cap) {
+  int c = p.context_lens[s];
+  return c < 0 ? 0 : (c > cap ? cap : c);
+}
+
+// Cascade decode: tokens of sequence s before this one belong to its group's
+// shared prefix (whole blocks, cut to its context); 0 for a plain decode.
+template <int BLK>
+__device__ __forceinline__ int shared_of(const DecodeParams& p, int s, int ctx) {
+  if (!p.shared_lens) return 0;
+  int l = p.shared_lens[s];
+  l = l < 0 ? 0 : l;
+  l -= l % BLK;  // whole blocks, then cut to the context (a short sequence ends inside them)
+  return l > ctx ? ctx : l;
+}
+
+// tokens the decode kernel covers: all of them, or those after the shared prefix
+template <int BLK>
+__device__ __forceinline__ int own_of(const DecodeParams& p, int s, int cap) {
+  const int c = ctx_of(p, s, cap);
+  return c - shared_of<BLK>(p, s, c);
+}
+
+// Wave-wide inclusive scan of one value per lane.
+__device__ __forceinline__ int wave_scan(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// One wave of the decode: logical wave index `logical` of the partition, on
+// lane `lane` (0..63) of a wave that runs nothing else.
+template <typename TQ, typename TC, int D, int BLK>
+__device__ __forceinline__ void decode_wave(const DecodeParams& p, const int logical, const int lane) {
+  typedef typename QFrag<TQ, TC, D>::T QT;
+  typedef ChunkRegs<TC, D> R;
+  constexpr int QS = QFrag<TQ, TC, D>::kSteps;
+  constexpr int NT = D / 16;  // output dim tiles
+  constexpr bool kSplitP = std::is_same<TQ, bf16_t>::value;  // bf16 P as hi + lo
+
+  const int hkc = logical / p.waves_per_head;  // kv head * head_chunks + chunk
+  const int w = logical % p.waves_per_head;
+  const int hk = hkc / p.head_chunks;
+  const int hchunk = hkc % p.head_chunks;
+  const int g = lane / 16, c16 = lane % 16;
+  const int cap = p.max_blocks * BLK;
+  const int nh = min(16, p.group - hchunk * 16);
+
+  // ---- partition: total chunks, this wave's range, its first sequence ----
+  int total = 0;
+  for (int b = 0; b < p.num_seqs; b += 64) {
+    const int s = b + lane;
+    int ch = s < p.num_seqs ? (own_of<BLK>(p, s, cap) + kChunk - 1) / kChunk : 0;
+    total += __shfl(wave_scan(ch, lane), 63);
+  }
+  total = __builtin_amdgcn_readfirstlane(total);
+  if (total == 0) return;
+  const int per_wave = (total + p.waves_per_head - 1) / p.waves_per_head;
+  const int c0 = w * per_wave;
+  const int c1 = min(c0 + per_wave, total);
+  // per-sequence partition info, written once for the combine kernel
+  if (logical == 0) {
+    int run = 0;
+    for (int b = 0; b < p.num_seqs; b += 64) {
+      const int s = b + lane;
+      int ch = s < p.num_seqs ? (own_of<BLK>(p, s, cap) + kChunk - 1) / kChunk : 0;
+      const int incl = run + wave_scan(ch, lane);
+      const int first = incl - ch;
+      if (s < p.num_seqs) {
+        p.seq_info[2 * s] = ch > 0 ? first / per_wave : 0;                                // first wave
+        p.seq_info[2 * s + 1] = ch > 0 ? (incl - 1) / per_wave - first / per_wave + 1 : 0;  // waves
+      }
+      run = __shfl(incl, 63);
+    }
+  }
+  if (c0 >= c1) return;
+  // first sequence of the range: the one whose chunks contain c0
+  int s_cur = 0, s_first_chunk = 0;
+  {
+    int run = 0;
+    for (int b = 0; b < p.num_seqs; b += 64) {
+      const int s = b + lane;
+      int ch = s < p.num_seqs ? (own_of<BLK>(p, s, cap) + kChunk - 1) / kChunk : 0;
+      const int incl = run + wave_scan(ch, lane);
+      const unsigned long long hit = __ballot(s < p.num_seqs && incl > c0);
+      if (hit) {
+        const int l0 = __builtin_ctzll(hit);
+        s_cur = b + l0;
+        s_first_chunk = __shfl(incl - ch, l0);
+        break;
+      }
+      run = __shfl(incl, 63);
+    }
+  }
+  s_cur = __builtin_amdgcn_readfirstlane(s_cur);
+  s_first_chunk = __builtin_amdgcn_readfirstlane(s_first_chunk);
+
+  const TC* kbase = reinterpret_cast<const TC*>(p.k_cache);
+  const TC* vbase = reinterpret_cast<const TC*>(p.v_cache);
+  const bool hvalid = c16 < nh;
+  const int qh_lane = hk * p.group + hchunk * 16 + (hvalid ? c16 : 0);
+
+  QT qf[QS];
+  f32x4 acc[NT];
+  float m_run, l_run;
+  // ctx counts this kernel's tokens of s_cur; bt starts at the first of them
+  auto table_of = [&](int s) {
+    return p.block_tables + (int64_t)s * p.bt_s0 + shared_of<BLK>(p, s, ctx_of(p, s, cap)) / BLK;
+  };
+  int ctx = own_of<BLK>(p, s_cur, cap);
+  int tb = (c0 - s_first_chunk) * kChunk;
+  const int32_t* bt = table_of(s_cur);
+
+  auto start_seq = [&]() {
+    load_q<TQ, TC, D>(qf, reinterpret_cast<const TQ*>(p.q) + s_cur * p.q_s0 + qh_lane * p.q_s1, hvalid, g);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
+  };
+
+  // write this wave's result for s_cur: final output if it saw the whole
+  // sequence, else an unnormalised partial in slot (w + s_cur)
+  auto finish_seq = [&](bool whole) {
+    float l = l_run + __shfl_xor(l_run, 16);
+    l += __shfl_xor(l, 32);
+    if (!hvalid) return;
+    const int qh = hk * p.group + hchunk * 16 + c16;
+    if (whole) {
+      const float inv = p.v_scale / l;
+      TQ* o = reinterpret_cast<TQ*>(p.out) + s_cur * p.o_s0 + qh * p.o_s1;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        typedef __attribute__((__vector_size__(4 * sizeof(TQ)))) TQ TQx4;
+        TQx4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = from_f32<TQ>(acc[n][i] * inv);
+        *reinterpret_cast<TQx4*>(o + 16 * n + 4 * g) = v;
+      }
+    } else {
+      const int64_t row = (int64_t)(w + s_cur) * p.hq + qh;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(p.ws_o + row * D + 16 * n + 4 * g) = acc[n];
+      if (g == 0) { p.ws_ml[row * 2] = m_run; p.ws_ml[row * 2 + 1] = l; }
+    }
+  };
+
+  start_seq();
+  int seq_start = s_first_chunk;  // global index of s_cur's first chunk
+  for (int c = c0; c < c1; ++c) {
+    // ---- load the chunk ----
+    const int jb = tb / BLK;
+    int b0 = bt[jb], b1 = b0;
+    if constexpr (BLK == 16) {
+      if ((jb + 1) * BLK < ctx) b1 = bt[jb + 1];  // only entries that hold live tokens
+    }
+    b0 = min(max(b0, 0), p.num_blocks - 1);
+    b1 = min(max(b1, 0), p.num_blocks - 1);
+    R r;
+    load_chunk<TC, D, BLK>(r, kbase, vbase, b0, b1, hk, p.hkv, c16, g);
+
+    // ---- scores S^T for 32 tokens: two 16-token tiles ----
+    float sc[8];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      f32x4 sv = score_tile<TQ, TC, D>(r, a, qf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[4 * a + i] = sv[i] * p.qk_scale_log2;
+    }
+    // lane (g, c16) holds tokens tb + 8g + j, j = 0..7, of head c16
+    const int nvalid = min(max(ctx - (tb + 8 * g), 0), 8);
+    const bool tail = tb + kChunk > ctx;
+    if (tail) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sc[j] = j < nvalid ? sc[j] : -INFINITY;
+    }
+    float cmax = sc[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, sc[j]);
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    const float m_new = fmaxf(m_run, cmax);
+    const float alpha = exp2f(m_run - m_new);
+    float pj[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { pj[j] = exp2f(sc[j] - m_new); psum += pj[j]; }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+
+    // ---- PV: O^T[d][head] += V^T[d][8 tokens] . P^T[8 tokens][head] ----
+    if constexpr (std::is_same<TC, float>::value) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float x = __builtin_bit_cast(float, r.v[n][j]);
+          x = (tail && j >= nvalid) ? 0.f : x;
+          acc[n] = mfma16x16x4(x, pj[j], acc[n]);
+        }
+      }
+    } else {
+      typedef typename Frag<TQ>::type F;
+      const F phi = pack8<TQ>(pj);
+      F plo;
+      if constexpr (kSplitP) {
+        float lo[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) lo[j] = pj[j] - (float)phi[j];  // exact in fp32
+        plo = pack8<TQ>(lo);
+      }
+      F vf[NT];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        if constexpr (std::is_same<TC, uint8_t>::value) vf[n] = fp8x8_to<TQ>(u32x2{r.v[n][0], r.v[n][1]});
+        else vf[n] = __builtin_bit_cast(F, u32x4{r.v[n][0], r.v[n][1], r.v[n][2], r.v[n][3]});
+      }
+      if (tail) {  // tokens past the end may hold anything (NaN): 0 * NaN is NaN
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) vf[n][j] = j < nvalid ? vf[n][j] : (TQ)0.f;
+      }
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        acc[n] = mfma16x16x32(vf[n], phi, acc[n]);
+        if constexpr (kSplitP) acc[n] = mfma16x16x32(vf[n], plo, acc[n]);
+      }
+    }
+
+    // ---- advance ----
+    tb += kChunk;
+    if (tb >= ctx || c + 1 == c1) {
+      const int nch = (ctx + kChunk - 1) / kChunk;
+      finish_seq(!p.shared_lens && seq_start >= c0 && seq_start + nch <= c1);  // cascade: always a partial
+      if (c + 1 == c1) break;
+      seq_start += nch;
+      do {  // next non-empty sequence
+        ++s_cur;
+        ctx = own_of<BLK>(p, s_cur, cap);
+      } while (ctx == 0);
+      tb = 0;
+      bt = table_of(s_cur);
+      start_seq();
+    }
+  }
+}
+
+}  // namespace
+}  // namespace pkv

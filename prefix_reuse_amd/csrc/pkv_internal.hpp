@@ -92,7 +92,15 @@ hipError_t launch_append(const AppendParams& p, DT row_dt, DT cache_dt, int head
                          int block_size, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, DT q_dt, DT cache_dt, int head_dim,
                          int block_size, hipStream_t stream);
+// the decode's combine kernel alone (after a cascade kernel wrote the partials)
+hipError_t launch_decode_combine(const DecodeParams& p, DT q_dt, DT cache_dt, int head_dim,
+                                 int block_size, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, DT q_dt, DT cache_dt, int head_dim,
                           int block_size, hipStream_t stream);
+// Cascade decode: the shared part (work-groups [0, shared_wgs), a multiple of
+// 8 and at least sp.hkv * sp.tiles_per_head) and the private-token decode
+// (dp.total_wgs waves, eight per work-group) in one launch, then the combine.
+hipError_t launch_cascade(const PrefillParams& sp, const DecodeParams& dp, int shared_wgs, DT q_dt, DT cache_dt,
+                          int head_dim, int block_size, hipStream_t stream);
 
 }  // namespace pkv
