@@ -84,3 +84,34 @@ def test_cascade_is_deterministic_and_ignores_physical_order():
     a = run_cascade(case)
     b = run_cascade(case)
     assert torch.equal(a, b)
+
+
+def test_cascade_many_groups():
+    """60 groups of 1-4 sequences: more shared-part work-groups than half the
+    CUs, so the decode waves get the smallest share of the device."""
+    rng = np.random.default_rng(630)
+    groups = []
+    for _ in range(60):
+        shared = int(rng.integers(0, 12)) * 16
+        lens = [int(x) for x in rng.integers(1, 300, int(rng.integers(1, 5)))]
+        groups.append((lens, shared))
+    case = workloads.make_grouped_decode_case(630, groups, 32, 8, 128, 16, torch.float16)
+    got = np64(run_cascade(case))
+    ref = oracle_decode(case)
+    assert report("cascade 60 groups", got, ref, torch.float16, TOL[torch.float16]) <= 1.0
+
+
+def test_cascade_long_shared_short_private():
+    """One group of 300 sequences on a 2,000-token prefix with 1-40 tokens of
+    their own: the shared part dominates the launch. Checked on every sequence
+    for 4 of the 32 heads."""
+    rng = np.random.default_rng(640)
+    lens = [2000 + int(x) for x in rng.integers(1, 41, 300)]
+    case = workloads.make_grouped_decode_case(640, [(lens, 2000)], 32, 8, 128, 32, torch.bfloat16)
+    got = np64(run_cascade(case))
+    heads = [0, 9, 18, 31]
+    ek, ev = oracle.append(np64(case.k_pool), np64(case.v_pool), np64(case.k_new), np64(case.v_new),
+                           case.slot_mapping.numpy())
+    ref = oracle.decode_attention(np64(case.q), ek, ev, case.block_tables.numpy(), case.context_lens.numpy(),
+                                  case.scale, heads=heads)
+    assert report("cascade long shared", got[:, heads], ref[:, heads], torch.bfloat16, TOL[torch.bfloat16]) <= 1.0

@@ -140,7 +140,7 @@ def _layout_sequences(g, lens, block_size, extra_free_blocks=0, shared=None):
     pool = used + extra_free_blocks
     perm = torch.randperm(pool, generator=g)
     poison = pool  # one extra all-NaN block after the pool proper
-    max_blocks = max(nblk_seq) if nseq else 1
+    max_blocks = max(max(nblk_seq) if nseq else 1, n_shared)  # every table holds the shared blocks
     bt = torch.full((nseq, max(max_blocks, 1)), poison, dtype=torch.int32)
     cursor = 0
     shared_ids = perm[:n_shared]
