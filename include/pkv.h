@@ -192,11 +192,10 @@ int pkv_suffix_prefill_attn(const pkv_tensor* q_suffix, const pkv_tensor* k_cach
  * pkv_cascade_workspace_bytes — bytes of device workspace pkv_cascade_decode_attn
  * needs on the CURRENT device: the decode workspace (rounded up to 16 bytes)
  * plus, for the shared part, one partial result per (key chunk, sequence,
- * query head): splits * num_seqs * H_q * (head_dim + 2) floats, where the
- * shared keys are cut into splits = min(4, max(1, CUs / row tiles)) chunks so
- * that the shared part fills more of the device (row tiles = H_kv *
- * ceil(num_seqs * G / 256)); the environment variable PKV_CASCADE_SPLITS
- * (1..16) replaces that count for both calls. Returns 0 on invalid sizes.
+ * query head): splits * num_seqs * H_q * (head_dim + 2) floats. The shared
+ * keys form one chunk (splits = 1) unless the environment variable
+ * PKV_CASCADE_SPLITS (1..16) sets another count, for both calls. Returns 0
+ * on invalid sizes.
  */
 size_t pkv_cascade_workspace_bytes(int64_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                    int32_t head_dim);
@@ -212,7 +211,8 @@ size_t pkv_cascade_workspace_bytes(int64_t num_seqs, int32_t num_q_heads, int32_
  * out[s, h] = softmax(scale * q[s,h] K_s^T) V_s over context_lens[s] tokens.
  * It is computed in two parts merged by log-sum-exp: for each group, all
  * queries of its sequences against its shared prefix at once (matrix cores),
- * and for each sequence the tokens after the shared prefix.
+ * and for each sequence the tokens after the shared prefix. Both parts run in
+ * one kernel launch, followed by a merge launch, on `stream`.
  *
  *  q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
  *  out           as for pkv_decode_attn; q and out must be f16 or bf16.
