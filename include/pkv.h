@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 
 typedef enum {
   PKV_F32 = 0,
@@ -157,6 +157,32 @@ int pkv_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_te
                     const pkv_tensor* block_tables, const pkv_tensor* context_lens, float scale,
                     float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
                     const pkv_tensor* out, void* stream);
+
+/*
+ * pkv_decode_step_attn — a whole decode step in one call: pkv_append of each
+ * sequence's newest token at position context_lens[s] - 1 (its slot taken
+ * from the block table), then pkv_decode_attn over context_lens[s] tokens.
+ * [C] §3: the new token's K, V join the cache and its query attends to all of
+ * them; [A] §02: position t lives in block block_tables[s][t / B] at offset
+ * t % B. The wave that reads the newest position takes its K, V from k_new /
+ * v_new and also writes them to the cache, so no separate append launch runs.
+ * Outputs and cache contents are bit for bit those of pkv_append (with
+ * slot_mapping[s] = that slot) followed by pkv_decode_attn.
+ *
+ *  k_new, v_new  [num_seqs, H_kv, d]: the newest token's K and V rows. Their
+ *                dtype is the cache dtype (copied bit for bit), or the q dtype
+ *                for an fp8 cache (stored as e4m3fn(x / k_scale), resp.
+ *                v_scale, as pkv_append stores it). Last dim contiguous, rows
+ *                16-byte aligned.
+ *  other args    as for pkv_decode_attn (same workspace size).
+ * A sequence with context_lens[s] <= 0 appends nothing and gets a zero row.
+ * The newest position's slot must not be one that another sequence of the
+ * same call reads (a block shared by several sequences is never appended to).
+ */
+int pkv_decode_step_attn(const pkv_tensor* q, const pkv_tensor* k_new, const pkv_tensor* v_new,
+                         const pkv_tensor* k_cache, const pkv_tensor* v_cache, const pkv_tensor* block_tables,
+                         const pkv_tensor* context_lens, float scale, float k_scale, float v_scale,
+                         void* workspace, size_t workspace_bytes, const pkv_tensor* out, void* stream);
 
 /*
  * pkv_suffix_prefill_attn — attention for the new suffix tokens of requests

@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "lib", "PkvError",
-    "append", "decode_attn", "suffix_prefill_attn", "decode_workspace_bytes",
+    "append", "decode_attn", "decode_step_attn", "suffix_prefill_attn", "decode_workspace_bytes",
     "cascade_decode_attn", "cascade_workspace_bytes",
     "empty_caches", "caches_from_logical", "k_logical", "v_logical", "abi_version",
 ]
@@ -64,6 +64,9 @@ def _load() -> ctypes.CDLL:
     L.pkv_decode_attn.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                   ctypes.c_void_p, ctypes.c_size_t, P, ctypes.c_void_p]
     L.pkv_decode_attn.restype = ctypes.c_int
+    L.pkv_decode_step_attn.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                       ctypes.c_void_p, ctypes.c_size_t, P, ctypes.c_void_p]
+    L.pkv_decode_step_attn.restype = ctypes.c_int
     L.pkv_suffix_prefill_attn.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_float,
                                           ctypes.c_float, P, ctypes.c_void_p]
     L.pkv_suffix_prefill_attn.restype = ctypes.c_int
@@ -170,19 +173,41 @@ def decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     """One paged decode step; returns ``out`` [num_seqs, H_q, d]."""
     if out is None:
         out = torch.empty_like(q)
-    block_size = k_cache.shape[2]
-    need = decode_workspace_bytes(q.shape[0], q.shape[1], k_cache.shape[1], q.shape[2],
-                                  block_tables.shape[1], block_size)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        # zero-filled once: the kernel's arrival counters start at 0 and are left at 0
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if (need and workspace is not None) else None
-    ws_bytes = workspace.numel() * workspace.element_size() if (need and workspace is not None) else 0
+    ws_ptr, ws_bytes = _decode_workspace(q, k_cache, block_tables, workspace)
     dq, dkc, dvc, dbt, dcl, do = map(_desc, (q, k_cache, v_cache, block_tables, context_lens, out))
     rc = lib.pkv_decode_attn(_ref(dq), _ref(dkc), _ref(dvc), _ref(dbt), _ref(dcl), float(scale),
                              float(k_scale), float(v_scale), ws_ptr, ws_bytes, _ref(do),
                              _stream(q.device))
     _check("pkv_decode_attn", rc)
+    return out
+
+
+def _decode_workspace(q, k_cache, block_tables, workspace):
+    need = decode_workspace_bytes(q.shape[0], q.shape[1], k_cache.shape[1], q.shape[2],
+                                  block_tables.shape[1], k_cache.shape[2])
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)  # no initial contents needed
+    if not need:
+        return None, 0
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def decode_step_attn(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                     v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                     scale: float, out: Optional[torch.Tensor] = None, k_scale: float = 1.0,
+                     v_scale: float = 1.0, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """A decode step in one call: each sequence's newest K/V row (k_new[s],
+    v_new[s]) goes to position context_lens[s] - 1 of the cache, and its query
+    attends to all context_lens[s] tokens; returns ``out``."""
+    if out is None:
+        out = torch.empty_like(q)
+    ws_ptr, ws_bytes = _decode_workspace(q, k_cache, block_tables, workspace)
+    dq, dkn, dvn, dkc, dvc, dbt, dcl, do = map(_desc, (q, k_new, v_new, k_cache, v_cache, block_tables,
+                                                        context_lens, out))
+    rc = lib.pkv_decode_step_attn(_ref(dq), _ref(dkn), _ref(dvn), _ref(dkc), _ref(dvc), _ref(dbt), _ref(dcl),
+                                  float(scale), float(k_scale), float(v_scale), ws_ptr, ws_bytes, _ref(do),
+                                  _stream(q.device))
+    _check("pkv_decode_step_attn", rc)
     return out
 
 

@@ -381,10 +381,14 @@ size_t pkv_decode_workspace_bytes(int64_t num_seqs, int32_t num_q_heads, int32_t
   return decode_ws_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, nullptr);
 }
 
-int pkv_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_tensor* v_cache,
-                    const pkv_tensor* block_tables, const pkv_tensor* context_lens, float scale,
-                    float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
-                    const pkv_tensor* out, void* stream) {
+}  // extern "C"
+
+namespace {
+// pkv_decode_attn, and with k_new / v_new (both or neither) pkv_decode_step_attn
+int decode_call(const pkv_tensor* q, const pkv_tensor* k_new, const pkv_tensor* v_new, const pkv_tensor* k_cache,
+                const pkv_tensor* v_cache, const pkv_tensor* block_tables, const pkv_tensor* context_lens,
+                float scale, float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                const pkv_tensor* out, void* stream) {
   int rc;
   CacheGeom cg;
   if ((rc = check_caches(k_cache, v_cache, &cg))) return rc;
@@ -408,9 +412,26 @@ int pkv_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_te
   if ((rc = check_block_tables(block_tables, S))) return rc;
   if ((rc = check_int_vector(context_lens, "context_lens", S))) return rc;
   if (!std::isfinite(scale)) return fail(PKV_ERR_SHAPE, "scale must be finite");
+  const bool step = k_new != nullptr || v_new != nullptr;
+  if (step) {
+    if ((rc = check_tensor(k_new, "k_new", 3))) return rc;
+    if ((rc = check_tensor(v_new, "v_new", 3))) return rc;
+    for (int i = 0; i < 3; ++i)
+      if (k_new->shape[i] != v_new->shape[i]) return fail(PKV_ERR_SHAPE, "k_new and v_new shapes differ");
+    if (k_new->shape[0] != S || k_new->shape[1] != cg.hkv || k_new->shape[2] != cg.dim)
+      return fail(PKV_ERR_SHAPE, "k_new/v_new must be [num_seqs=%lld, H_kv=%d, d=%d]", (long long)S, cg.hkv, cg.dim);
+    const int want = fp8 ? q->dtype : cg.dtype;
+    if (k_new->dtype != want || v_new->dtype != want)
+      return fail(PKV_ERR_DTYPE, "k_new/v_new must be %s (%s)", dtype_name(want),
+                  fp8 ? "the q dtype, quantized into the fp8 cache" : "the cache dtype, copied bit for bit");
+  }
   if (S == 0) return ok();
   if ((rc = check_rows(q, "q"))) return rc;
   if ((rc = check_rows(out, "out"))) return rc;
+  if (step) {
+    if ((rc = check_rows(k_new, "k_new"))) return rc;
+    if ((rc = check_rows(v_new, "v_new"))) return rc;
+  }
 
   pkv::DecodePlan plan;
   const size_t need = decode_ws_bytes(S, (int32_t)hq, cg.hkv, cg.dim, &plan);
@@ -435,9 +456,36 @@ int pkv_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_te
   p.seq_info = reinterpret_cast<int32_t*>(p.ws_ml + slots * hq * 2);
   p.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * pkv::kLog2eHost;
   p.v_scale = fp8 ? v_scale : 1.0f;
+  if (step) {
+    p.k_new = k_new->data; p.kn_s0 = k_new->stride[0]; p.kn_s1 = k_new->stride[1];
+    p.v_new = v_new->data; p.vn_s0 = v_new->stride[0]; p.vn_s1 = v_new->stride[1];
+    p.k_quant = k_scale;
+    p.v_quant = v_scale;
+  }
   hipError_t e = pkv::launch_decode(p, to_dt(q->dtype), to_dt(cg.dtype), cg.dim, cg.block, (hipStream_t)stream);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+}  // namespace
+
+extern "C" {
+
+int pkv_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_tensor* v_cache,
+                    const pkv_tensor* block_tables, const pkv_tensor* context_lens, float scale,
+                    float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                    const pkv_tensor* out, void* stream) {
+  return decode_call(q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
+                     workspace, workspace_bytes, out, stream);
+}
+
+int pkv_decode_step_attn(const pkv_tensor* q, const pkv_tensor* k_new, const pkv_tensor* v_new,
+                         const pkv_tensor* k_cache, const pkv_tensor* v_cache, const pkv_tensor* block_tables,
+                         const pkv_tensor* context_lens, float scale, float k_scale, float v_scale, void* workspace,
+                         size_t workspace_bytes, const pkv_tensor* out, void* stream) {
+  if (!k_new) return fail(PKV_ERR_NULL, "k_new: descriptor is NULL");
+  if (!v_new) return fail(PKV_ERR_NULL, "v_new: descriptor is NULL");
+  return decode_call(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
+                     workspace, workspace_bytes, out, stream);
 }
 
 int pkv_suffix_prefill_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_tensor* v_cache,

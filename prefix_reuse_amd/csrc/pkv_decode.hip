@@ -38,9 +38,12 @@
 namespace pkv {
 namespace {
 
-template <typename TQ, typename TC, int D, int BLK>
-__global__ __launch_bounds__(64, 3) void decode_kernel(DecodeParams p) {
-  decode_wave<TQ, TC, D, BLK>(p, xcd_remap(blockIdx.x, p.total_wgs), threadIdx.x);
+// kStep: the decode step's form, which also appends each sequence's newest
+// token (DecodeParams::k_new). It needs more registers than the 168 that three
+// waves per SIMD allow; the partition runs two per SIMD anyway.
+template <typename TQ, typename TC, int D, int BLK, bool kStep>
+__global__ __launch_bounds__(64, kStep ? 2 : 3) void decode_kernel(DecodeParams p) {
+  decode_wave<TQ, TC, D, BLK, kStep>(p, xcd_remap(blockIdx.x, p.total_wgs), threadIdx.x);
 }
 
 // Merge the partials of the sequences that several waves shared, in wave
@@ -181,7 +184,10 @@ hipError_t launch_combine_typed(const DecodeParams& p, hipStream_t stream) {
 template <typename TQ, typename TC, int D, int BLK>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t stream, bool combine_only) {
   if (!combine_only) {
-    hipLaunchKernelGGL((decode_kernel<TQ, TC, D, BLK>), dim3(p.total_wgs), dim3(64), 0, stream, p);
+    if (p.k_new)
+      hipLaunchKernelGGL((decode_kernel<TQ, TC, D, BLK, true>), dim3(p.total_wgs), dim3(64), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_kernel<TQ, TC, D, BLK, false>), dim3(p.total_wgs), dim3(64), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -93,6 +93,129 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<TC, D>& r, const TC* kbase,
   }
 }
 
+// Decode step: the chunk's token jn (0..31, uniform) is the sequence's newest
+// one. Its K and V come from the step's rows instead of the cache, converted
+// exactly as pkv_append converts them (bit copy; for fp8, e4m3fn(x / scale)).
+// fetch_new_token issues their loads before the chunk's own (both arrive in
+// one round trip), place_new_token swaps the values into the chunk registers,
+// and store_new_token writes them to the cache slot that the chunk load read,
+// so the cache ends as an append would leave it.
+template <typename TQ, typename TC, int D>
+struct NewToken {
+  static constexpr bool kFp8 = std::is_same<TC, uint8_t>::value;
+  typedef typename std::conditional<kFp8, TQ, TC>::type TR;  // dtype of the step's rows
+  static constexpr int KN = ChunkRegs<TC, D>::KN;
+  static constexpr int NT = ChunkRegs<TC, D>::NT;
+  u32x4 k[KN][kFp8 ? 2 : 1];  // this lane's K pieces as raw row bytes (fp8: 16 row values each)
+  TR v[NT];                   // this lane's V values (dims c16 + 16n)
+  uint32_t vbits[NT];         // the same as the cache stores them
+  int a;                      // which A row of the lane is token jn (-1: none)
+  int jv;                     // element of the lane's V pieces that is token jn (-1: none)
+};
+
+template <typename TQ, typename TC, int D>
+__device__ __forceinline__ void fetch_new_token(NewToken<TQ, TC, D>& nt, const DecodeParams& p, int s, int jn, int hk,
+                                                int c16, int g) {
+  typedef NewToken<TQ, TC, D> N;
+  typedef typename N::TR TR;
+  constexpr int E = ChunkRegs<TC, D>::E;
+  const TR* knew = reinterpret_cast<const TR*>(p.k_new) + (int64_t)s * p.kn_s0 + (int64_t)hk * p.kn_s1;
+  const TR* vnew = reinterpret_cast<const TR*>(p.v_new) + (int64_t)s * p.vn_s0 + (int64_t)hk * p.vn_s1;
+  nt.a = -1;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+    if (8 * (c16 / 4) + 4 * a + (c16 % 4) == jn) nt.a = a;
+  if (nt.a >= 0) {
+#pragma unroll
+    for (int c = 0; c < N::KN; ++c) {
+      const TR* src = knew + g * E + c * 4 * E;
+#pragma unroll
+      for (int h = 0; h < (N::kFp8 ? 2 : 1); ++h) nt.k[c][h] = load_u32x4(src + h * (16 / sizeof(TR)));
+    }
+  }
+  nt.jv = jn - 8 * g;
+  if (nt.jv < 0 || nt.jv >= 8) nt.jv = -1;
+  if (nt.jv >= 0) {
+#pragma unroll
+    for (int n = 0; n < N::NT; ++n) nt.v[n] = vnew[c16 + 16 * n];
+  }
+}
+
+// Converts the fetched values in place (nt.k to the cache's K bytes, nt.v to
+// the cache's V values as raw bits) and swaps them into the chunk registers.
+template <typename TQ, typename TC, int D>
+__device__ __forceinline__ void place_new_token(ChunkRegs<TC, D>& r, NewToken<TQ, TC, D>& nt,
+                                                const DecodeParams& p) {
+  typedef ChunkRegs<TC, D> R;
+  typedef NewToken<TQ, TC, D> N;
+  typedef typename N::TR TR;
+  if (nt.a >= 0) {
+#pragma unroll
+    for (int c = 0; c < R::KN; ++c) {
+      u32x4 w;
+      if constexpr (N::kFp8) {
+        typedef __attribute__((__vector_size__(8 * sizeof(TR)))) TR TR8;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const TR8 x = __builtin_bit_cast(TR8, nt.k[c][q / 2]);
+          uint32_t word = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) word |= f32_to_e4m3fn(to_f32(x[4 * (q % 2) + j]) / p.k_quant) << (8 * j);
+          w[q] = word;
+        }
+      } else {
+        w = nt.k[c][0];
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        if (a == nt.a) r.k[a][c] = w;
+      nt.k[c][0] = w;
+    }
+  }
+  if (nt.jv < 0) return;
+  constexpr int kBits = 8 * sizeof(TC);
+  constexpr int kPerWord = 32 / kBits;
+  constexpr uint32_t kMask = kBits == 32 ? 0xffffffffu : ((1u << kBits) - 1u);
+#pragma unroll
+  for (int n = 0; n < R::NT; ++n) {
+    uint32_t bits;
+    if constexpr (N::kFp8) bits = f32_to_e4m3fn(to_f32(nt.v[n]) / p.v_quant);
+    else if constexpr (kBits == 16) bits = __builtin_bit_cast(uint16_t, nt.v[n]);
+    else bits = __builtin_bit_cast(uint32_t, nt.v[n]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {  // static register indices; one of them is jv
+      if (j != nt.jv) continue;
+      const int sh = kBits * (j % kPerWord);
+      r.v[n][j / kPerWord] = (r.v[n][j / kPerWord] & ~(kMask << sh)) | (bits << sh);
+    }
+    nt.vbits[n] = bits;
+  }
+}
+
+// Writes the placed values to the newest token's cache slot. Issued after the
+// chunk's products, when the chunk's own loads of those lines have returned.
+template <typename TQ, typename TC, int D, int BLK>
+__device__ __forceinline__ void store_new_token(const NewToken<TQ, TC, D>& nt, const DecodeParams& p, int jn,
+                                                TC* kbase, TC* vbase, int blk0, int blk1, int hk, int c16, int g) {
+  typedef ChunkRegs<TC, D> R;
+  const int64_t tile = (int64_t)BLK * D;
+  if (nt.a >= 0) {
+    const int blk = (BLK == 32 || jn < 16) ? blk0 : blk1;
+    TC* kdst = kbase + ((int64_t)blk * p.hkv + hk) * tile + (int64_t)(jn % BLK) * D + g * R::E;
+#pragma unroll
+    for (int c = 0; c < R::KN; ++c) *reinterpret_cast<u32x4*>(kdst + c * 4 * R::E) = nt.k[c][0];
+  }
+  if (nt.jv < 0) return;
+  const int tokv = 8 * g;
+  const int blkv = (BLK == 32 || tokv < 16) ? blk0 : blk1;
+  TC* vt = vbase + ((int64_t)blkv * p.hkv + hk) * tile + (tokv % BLK) + (int64_t)c16 * BLK;
+  constexpr int kBits = 8 * sizeof(TC);
+  typedef typename std::conditional<kBits == 8, uint8_t,
+                                    typename std::conditional<kBits == 16, uint16_t, uint32_t>::type>::type UT;
+#pragma unroll
+  for (int n = 0; n < R::NT; ++n) reinterpret_cast<UT*>(vt)[(int64_t)16 * n * BLK + nt.jv] = (UT)nt.vbits[n];
+}
+
 // Scores of the 16-token tile a from loaded K rows: result element i is the
 // score of chunk token 8g + 4a + i for head c16.
 template <typename TQ, typename TC, int D, typename QT>
@@ -159,7 +282,7 @@ __device__ __forceinline__ int wave_scan(int x, int lane) {
 
 // One wave of the decode: logical wave index `logical` of the partition, on
 // lane `lane` (0..63) of a wave that runs nothing else.
-template <typename TQ, typename TC, int D, int BLK>
+template <typename TQ, typename TC, int D, int BLK, bool kStep = false>
 __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int logical, const int lane) {
   typedef typename QFrag<TQ, TC, D>::T QT;
   typedef ChunkRegs<TC, D> R;
@@ -286,7 +409,15 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int log
     b0 = min(max(b0, 0), p.num_blocks - 1);
     b1 = min(max(b1, 0), p.num_blocks - 1);
     R r;
+    const int jn = ctx - 1 - tb;  // decode step: the newest token, if this chunk holds it
+    NewToken<TQ, TC, D> nt;
+    if constexpr (kStep) {
+      if (jn < kChunk) fetch_new_token<TQ, TC, D>(nt, p, s_cur, jn, hk, c16, g);
+    }
     load_chunk<TC, D, BLK>(r, kbase, vbase, b0, b1, hk, p.hkv, c16, g);
+    if constexpr (kStep) {
+      if (jn < kChunk) place_new_token<TQ, TC, D>(r, nt, p);
+    }
 
     // ---- scores S^T for 32 tokens: two 16-token tiles ----
     float sc[8];
@@ -357,6 +488,11 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int log
         acc[n] = mfma16x16x32(vf[n], phi, acc[n]);
         if constexpr (kSplitP) acc[n] = mfma16x16x32(vf[n], plo, acc[n]);
       }
+    }
+
+    if constexpr (kStep) {
+      if (jn < kChunk && hchunk == 0)
+        store_new_token<TQ, TC, D, BLK>(nt, p, jn, const_cast<TC*>(kbase), const_cast<TC*>(vbase), b0, b1, hk, c16, g);
     }
 
     // ---- advance ----

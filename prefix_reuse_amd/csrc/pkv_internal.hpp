@@ -44,6 +44,13 @@ struct DecodeParams {
   const float* sh_o;                  // [sh_splits, S, Hq, D]: one partial per key split
   const float* sh_ml;                 // [sh_splits, S, Hq, 2]
   int32_t sh_splits;
+  // decode step (nullptr otherwise): the newest token of each sequence,
+  // [S, Hkv, D] in the cache dtype (in the q dtype for an fp8 cache), at
+  // position context_lens[s] - 1. The wave that reads that position takes it
+  // from here and writes it into the cache slot, as pkv_append would.
+  const void* k_new; const void* v_new;
+  int64_t kn_s0, kn_s1, vn_s0, vn_s1;
+  float k_quant, v_quant;             // fp8: code = e4m3fn(x / scale)
 };
 
 // Suffix-prefill work-group: kPrefillWaves waves of 32 (token, head) rows each.

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert pkv.abi_version() == 2
+    assert pkv.abi_version() == 3
 
 
 def T(shape, dtype, strides=None, ptr=FAKE):
@@ -191,3 +191,24 @@ def test_cascade_workspace_size_formula(monkeypatch):
     monkeypatch.setenv("PKV_CASCADE_SPLITS", "3")
     dec = pkv.decode_workspace_bytes(5, 32, 8, 128, 100, 32)
     assert pkv.cascade_workspace_bytes(5, 32, 8, 128) == (dec + 15) // 16 * 16 + 3 * 5 * 32 * 130 * 4
+
+
+def step(q, kn, vn, kc, vc, bt, cl, out, ws=None, ws_bytes=0, scale=0.125, ks=1.0, vs=1.0):
+    return pkv.lib.pkv_decode_step_attn(R(q), R(kn), R(vn), R(kc), R(vc), R(bt), R(cl), scale, ks, vs, ws, ws_bytes,
+                                        R(out), None)
+
+
+def test_decode_step_rejects_bad_new_rows():
+    kc, vc = caches()
+    q, out, bt, cl = T([2, 4, 64], F16), T([2, 4, 64], F16), T([2, 4], I32), T([2], I32)
+    good = T([2, 2, 64], F16)
+    assert step(q, None, good, kc, vc, bt, cl, out) == 1 and "k_new" in err()
+    assert step(q, good, None, kc, vc, bt, cl, out) == 1 and "v_new" in err()
+    assert step(q, T([2, 2, 64], F32), good, kc, vc, bt, cl, out) == 2 and "cache dtype" in err()
+    assert step(q, T([3, 2, 64], F16), T([3, 2, 64], F16), kc, vc, bt, cl, out) == 3
+    assert step(q, T([2, 2, 64], F16), T([2, 1, 64], F16), kc, vc, bt, cl, out) == 3
+    assert step(q, T([2, 2, 64], F16, ptr=FAKE + 2), good, kc, vc, bt, cl, out) == 4
+    # an fp8 cache takes the rows in the q dtype, quantized like pkv_append
+    kc8, vc8 = caches(dt=FP8)
+    assert step(q, good, good, kc8, vc8, bt, cl, out) == 6  # rows accepted; no workspace given
+    assert step(T([2, 4, 64], BF16), good, good, kc8, vc8, bt, cl, T([2, 4, 64], BF16)) == 2 and "q dtype" in err()
