@@ -115,3 +115,26 @@ def test_cascade_long_shared_short_private():
     ref = oracle.decode_attention(np64(case.q), ek, ev, case.block_tables.numpy(), case.context_lens.numpy(),
                                   case.scale, heads=heads)
     assert report("cascade long shared", got[:, heads], ref[:, heads], torch.bfloat16, TOL[torch.bfloat16]) <= 1.0
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_cascade_random_groupings(seed):
+    """Seeded random batches: 1-12 groups of 1-9 sequences, shared prefixes of
+    0-20 blocks, own lengths 0-400, random dtype, head dim, block size and GQA
+    grouping."""
+    rng = np.random.default_rng(900 + seed)
+    b = int(rng.choice([16, 32]))
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8]))
+    dtype = [torch.float16, torch.bfloat16][int(rng.integers(2))]
+    groups = []
+    for _ in range(int(rng.integers(1, 13))):
+        shared = int(rng.integers(0, 21)) * b
+        lens = [shared + int(x) for x in rng.integers(-shared // 2 if shared else 0, 401, int(rng.integers(1, 10)))]
+        groups.append(([max(x, 0) for x in lens], shared))
+    case = workloads.make_grouped_decode_case(900 + seed, groups, hq, hkv, d, b, dtype)
+    print(f"seed {seed}: {len(groups)} groups, {case.num_seqs} seqs, {dtype} d={d} B={b} {hq}/{hkv}", flush=True)
+    got = np64(run_cascade(case))
+    ref = oracle_decode(case)
+    assert report(f"cascade random {seed}", got, ref, dtype, TOL[dtype]) <= 1.0

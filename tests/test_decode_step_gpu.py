@@ -86,3 +86,22 @@ def test_step_rejects_bad_rows():
         pkv.decode_step_attn(args[0], args[1].float(), *args[2:])  # dtype differs from the cache
     with pytest.raises(pkv.PkvError):
         pkv.decode_step_attn(args[0], args[1][:1], args[2][:1], *args[3:])  # one row for two sequences
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_step_random_batches(seed):
+    """Seeded random batches (1-80 sequences of 0-3,000 tokens, random dtype,
+    head dim, block size and GQA grouping up to 32): bit for bit against
+    append + decode."""
+    rng = np.random.default_rng(950 + seed)
+    b = int(rng.choice([16, 32]))
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    hq = hkv * int(rng.choice([1, 4, 8, 32]))
+    dtype = [torch.float32, torch.float16, torch.bfloat16][int(rng.integers(3))]
+    lens = [int(x) for x in rng.integers(0, 3001, int(rng.integers(1, 81)))]
+    case = workloads.make_decode_case(950 + seed, lens, hq, hkv, d, b, dtype)
+    print(f"seed {seed}: {len(lens)} seqs, {dtype} d={d} B={b} {hq}/{hkv}", flush=True)
+    kc0, vc0 = pkv.caches_from_logical(case.k_pool, case.v_pool, "cuda")
+    a, s = two_ways(case, kc0, vc0, case.q.cuda(), case.k_new.cuda(), case.v_new.cuda())
+    assert_same(a, s)
