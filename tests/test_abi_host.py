@@ -212,3 +212,21 @@ def test_decode_step_rejects_bad_new_rows():
     kc8, vc8 = caches(dt=FP8)
     assert step(q, good, good, kc8, vc8, bt, cl, out) == 6  # rows accepted; no workspace given
     assert step(T([2, 4, 64], BF16), good, good, kc8, vc8, bt, cl, T([2, 4, 64], BF16)) == 2 and "q dtype" in err()
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without libpkv.so the package refuses to import: there is no CPU path to
+    fall back to."""
+    import shutil
+    import subprocess
+    import sys
+
+    pkg = tmp_path / "prefix_reuse_amd"
+    pkg.mkdir()
+    src = Path(pkv.__file__).parent
+    for f in src.glob("*.py"):
+        shutil.copy(f, pkg / f.name)  # the package without its built library
+    res = subprocess.run([sys.executable, "-c", "import prefix_reuse_amd"], cwd=tmp_path, capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode != 0
+    assert "ImportError" in res.stderr and "There is no CPU fallback" in res.stderr
