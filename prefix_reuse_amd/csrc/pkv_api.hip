@@ -358,6 +358,9 @@ int pkv_append(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* slot_
   if (T == 0) return ok();
   if ((rc = check_rows(k, "k"))) return rc;
   if ((rc = check_rows(v, "v"))) return rc;
+  // two threads per (row, KV head, 8 dims), at most 2^31 - 1 work-groups of 256
+  if (T > ((int64_t)1 << 37) / ((int64_t)cg.hkv * (cg.dim / 8)))
+    return fail(PKV_ERR_SHAPE, "too many rows (%lld) for one append", (long long)T);
 
   pkv::AppendParams p{};
   p.k = k->data; p.v = v->data;
