@@ -493,6 +493,10 @@ def main() -> int:
                          "avg_launch_us": round(pre_ms * 1e3, 2)},
             "suffix_tokens_per_s": round(int(pc.suffix_lens.sum()) / (pre_ms * 1e-3), 1),
         }
+        # the pages' flow: append the suffix K/V, then the prefill
+        flow_ms = time_launches(torch, stream, lambda: (pkv.append(p["k_new"], p["v_new"], p["slots"], p["kc"], p["vc"]),
+                                                        run_prefill_call(pkv, p)), args.steps)
+        result["suffix_prefill"]["append_then_prefill_us"] = round(flow_ms * 1e3, 2)
         del p
         torch.cuda.empty_cache()
         # the same prefill over an fp8 e4m3fn cache (multi-turn with an fp8 KV cache)
