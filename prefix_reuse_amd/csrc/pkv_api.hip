@@ -272,9 +272,10 @@ int pkv_cascade_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, cons
     sp.num_reqs = (int32_t)G; sp.hq = (int32_t)hq; sp.hkv = cg.hkv; sp.group = (int32_t)(hq / cg.hkv);
     sp.num_blocks = (int32_t)cg.num_blocks; sp.total_rows = S;
     constexpr int64_t W = pkv::kPrefillRowsPerWg;
-    // an upper bound on the row tiles (each group's last one may be partial);
-    // work-groups past a group list's real tiles return at once
-    const int64_t tiles = ((S * sp.group + W - 1) / W + G) * splits;
+    // the row tiles of all groups: sum_g ceil(n_g G / W) <= floor(S G / W) + G
+    // (exact for one group); work-groups past the real tiles return at once
+    const int64_t rows = S * sp.group;
+    const int64_t tiles = (G == 1 ? (rows + W - 1) / W : rows / W + G) * splits;
     if (tiles * cg.hkv > INT32_MAX / 2) return fail(PKV_ERR_SHAPE, "problem too large for one launch");
     sp.tiles_per_head = (int32_t)tiles;
     sp.key_splits = splits;
