@@ -70,14 +70,16 @@ __global__ __launch_bounds__(kCombineHeads * D / 4) void decode_combine_kernel(D
   const int first = p.seq_info[2 * seq];
   int n = p.seq_info[2 * seq + 1];
   constexpr int kMaxSplits = 16;
-  f32x2 sml[kMaxSplits];
-  f32x4 so[kMaxSplits];
+  // the first shared partial; a shared prefix cut into several key chunks has
+  // more, merged further down in batches
+  f32x2 sml0 = f32x2{-INFINITY, 0.f};
+  f32x4 so0 = f32x4{0.f, 0.f, 0.f, 0.f};
   int lr = 0;
   if (p.shared_lens) {
     lr = p.shared_lens[seq];
     const int64_t srow = (int64_t)seq * p.hq + qh;
-    sml[0] = *reinterpret_cast<const f32x2*>(p.sh_ml + srow * 2);
-    so[0] = *reinterpret_cast<const f32x4*>(p.sh_o + srow * D + d0);
+    sml0 = *reinterpret_cast<const f32x2*>(p.sh_ml + srow * 2);
+    so0 = *reinterpret_cast<const f32x4*>(p.sh_o + srow * D + d0);
   }
   if (ctx == 0) {
     TQx4 z;
@@ -102,21 +104,10 @@ __global__ __launch_bounds__(kCombineHeads * D / 4) void decode_combine_kernel(D
     nsh = chunk > 0 ? min((sh + chunk - 1) / chunk, min(p.sh_splits, kMaxSplits)) : 0;
   }
   if (nsh < 1) {
-    sml[0] = f32x2{-INFINITY, 0.f};
-    so[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    sml0 = f32x2{-INFINITY, 0.f};
+    so0 = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-#pragma unroll
-  for (int i = 1; i < kMaxSplits; ++i) {
-    sml[i] = f32x2{-INFINITY, 0.f};
-    so[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (i < nsh) {
-      const int64_t srow = ((int64_t)i * p.num_seqs + seq) * p.hq + qh;
-      sml[i] = *reinterpret_cast<const f32x2*>(p.sh_ml + srow * 2);
-      so[i] = *reinterpret_cast<const f32x4*>(p.sh_o + srow * D + d0);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kMaxSplits; ++i) M = fmaxf(M, sml[i][0]);
+  M = sml0[0];
   // one round of loads for up to kFew partials, then a general loop
   constexpr int kFew = 8;
   const int nf = n < kFew ? n : kFew;
@@ -130,11 +121,10 @@ __global__ __launch_bounds__(kCombineHeads * D / 4) void decode_combine_kernel(D
   }
 #pragma unroll
   for (int i = 0; i < kFew; ++i) M = fmaxf(M, ml[i][0]);
-#pragma unroll
-  for (int i = 0; i < kMaxSplits; ++i) {
-    const float f = i < nsh ? exp2f(sml[i][0] - M) : 0.f;
-    L += sml[i][1] * f;
-    O += so[i] * f;
+  if (nsh >= 1) {
+    const float f = exp2f(sml0[0] - M);
+    L += sml0[1] * f;
+    O += so0 * f;
   }
 #pragma unroll
   for (int i = 0; i < kFew; ++i) {
@@ -142,8 +132,32 @@ __global__ __launch_bounds__(kCombineHeads * D / 4) void decode_combine_kernel(D
     L += ml[i][1] * f;
     O += o[i] * f;
   }
-  // further partials (long contexts spread over many waves) in batches of
-  // kFew, each loaded in one round and merged under a running maximum
+  // further partials in batches of kFew, each loaded in one round and merged
+  // under a running maximum: the other shared chunks, then the partials of a
+  // long context spread over many waves. A batch only moves the maximum up
+  // (r = 1 while both are still -inf: nothing has been added yet).
+  for (int i0 = 1; i0 < nsh; i0 += kFew) {
+#pragma unroll
+    for (int i = 0; i < kFew; ++i) {
+      const int64_t srow = ((int64_t)(i0 + i) * p.num_seqs + seq) * p.hq + qh;
+      const bool ok = i0 + i < nsh;
+      ml[i] = ok ? *reinterpret_cast<const f32x2*>(p.sh_ml + srow * 2) : f32x2{-INFINITY, 0.f};
+      o[i] = ok ? *reinterpret_cast<const f32x4*>(p.sh_o + srow * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < kFew; ++i) Mb = fmaxf(Mb, ml[i][0]);
+    const float r = M == Mb ? 1.f : exp2f(M - Mb);
+    L *= r;
+    O *= r;
+    M = Mb;
+#pragma unroll
+    for (int i = 0; i < kFew; ++i) {
+      const float f = i0 + i < nsh ? exp2f(ml[i][0] - M) : 0.f;
+      L += ml[i][1] * f;
+      O += o[i] * f;
+    }
+  }
   for (int i0 = kFew; i0 < n; i0 += kFew) {
 #pragma unroll
     for (int i = 0; i < kFew; ++i) {
@@ -155,7 +169,7 @@ __global__ __launch_bounds__(kCombineHeads * D / 4) void decode_combine_kernel(D
     float Mb = M;
 #pragma unroll
     for (int i = 0; i < kFew; ++i) Mb = fmaxf(Mb, ml[i][0]);
-    const float r = exp2f(M - Mb);  // M is finite: the first round held a partial
+    const float r = M == Mb ? 1.f : exp2f(M - Mb);
     L *= r;
     O *= r;
     M = Mb;

@@ -138,3 +138,17 @@ def test_cascade_random_groupings(seed):
     got = np64(run_cascade(case))
     ref = oracle_decode(case)
     assert report(f"cascade random {seed}", got, ref, dtype, TOL[dtype]) <= 1.0
+
+
+@pytest.mark.parametrize("splits", [2, 3, 9, 16])
+def test_cascade_shared_keys_in_several_chunks(splits, monkeypatch):
+    """The shared keys cut into 2-16 chunks, each a work-group of its own whose
+    partial joins the merge: 9 and 16 chunks take the merge past its first
+    batch of eight partials. Members shorter than the prefix see fewer chunks."""
+    monkeypatch.setenv("PKV_CASCADE_SPLITS", str(splits))
+    groups = [([1100, 1300, 1050, 1500, 700, 40], 1024), ([60, 90], 32), ([300], 0)]
+    case = workloads.make_grouped_decode_case(650, groups, 16, 4, 128, 32, torch.bfloat16)
+    print(f"cascade with {splits} shared key chunks", flush=True)
+    got = np64(run_cascade(case))
+    ref = oracle_decode(case)
+    assert report(f"cascade {splits} chunks", got, ref, torch.bfloat16, TOL[torch.bfloat16]) <= 1.0
