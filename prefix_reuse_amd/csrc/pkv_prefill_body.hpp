@@ -684,6 +684,10 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
   // A converted bf16 cache's V stage `cst` (the next one, no tail) is
   // converted here too: the thread's piece t is read first, converted a word
   // at a time between the score products and written back at the end.
+  // A thread converts the same pieces (t * kThreads + tid) here as in
+  // convert_v: waves of one work-group can run different loops during the
+  // same stage (their full-step counts differ), and every piece must be
+  // converted exactly once.
   auto step_full = [&](int bk, int bv, int t, const PFrag<FV>& pcur, PFrag<FV>& pnext, VOps& vo, KOps& ko,
                        bool next, int cst) {
     if constexpr (!T::kSplitP) {  // one value product per operand
