@@ -687,7 +687,9 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
   // A thread converts the same pieces (t * kThreads + tid) here as in
   // convert_v: waves of one work-group can run different loops during the
   // same stage (their full-step counts differ), and every piece must be
-  // converted exactly once.
+  // converted exactly once. Those pieces lie in the 1 KB chunks that the
+  // thread's own wave loads, which lets the prologue convert V stage 0 after
+  // its own loads' wait, with no barrier.
   auto step_full = [&](int bk, int bv, int t, const PFrag<FV>& pcur, PFrag<FV>& pnext, VOps& vo, KOps& ko,
                        bool next, int cst) {
     if constexpr (!T::kSplitP) {  // one value product per operand
