@@ -62,7 +62,11 @@ int check_tensor(const pkv_tensor* t, const char* name, int ndim) {
   for (int i = 0; i < ndim; ++i)
     if (t->shape[i] < 0) return fail(PKV_ERR_SHAPE, "%s: negative extent in dim %d", name, i);
   int64_t numel = 1;
-  for (int i = 0; i < ndim; ++i) numel *= t->shape[i];
+  for (int i = 0; i < ndim; ++i) {
+    if (t->shape[i] > 0 && numel > INT64_MAX / t->shape[i])
+      return fail(PKV_ERR_SHAPE, "%s: element count overflows 64 bits", name);
+    numel *= t->shape[i];
+  }
   if (numel > 0 && !t->data) return fail(PKV_ERR_NULL, "%s: data pointer is NULL", name);
   return PKV_OK;
 }

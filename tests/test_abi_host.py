@@ -72,6 +72,15 @@ def test_decode_rejects_null_descriptor():
     assert rc == 1 and "q" in err()
 
 
+def test_element_count_overflow_is_rejected():
+    """Extents whose product overflows 64 bits fail validation (status SHAPE)
+    instead of wrapping around into a plausible size."""
+    kc, vc = caches()
+    huge = T([2 ** 40, 2 ** 40, 64], F16, strides=[2 ** 46, 64, 1])
+    rc = decode(huge, kc, vc, T([2, 4], I32), T([2], I32), T([2, 4, 64], F16))
+    assert rc == 3 and "overflows" in err()
+
+
 def test_decode_rejects_group_mismatch():
     kc, vc = caches(h=3)
     rc = decode(T([2, 4, 64], F16), kc, vc, T([2, 4], I32), T([2], I32), T([2, 4, 64], F16))
