@@ -113,6 +113,11 @@ def _ref(d):
 def _stream(device: torch.device) -> int:
     if device.type != "cuda":
         raise ValueError("tensors must live on a GPU")
+    # the library launches on the current HIP device, so the tensors must be there
+    current = torch.cuda.current_device()
+    if device.index is not None and device.index != current:
+        raise ValueError(f"tensors live on cuda:{device.index} but the current device is cuda:{current}; "
+                         f"call under torch.cuda.device({device.index})")
     return torch.cuda.current_stream(device).cuda_stream
 
 
