@@ -260,16 +260,65 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     split = tile % p.key_splits;
     tile /= p.key_splits;
   }
-  int r = 0, row_base = 0, rows_r = 0;
-  for (; r < p.num_reqs; ++r) {
-    int s = casc ? p.group_starts[r + 1] - p.group_starts[r] : p.suffix_lens[r];
-    s = s < 0 ? 0 : s;
-    if (row_base + s > p.total_rows) s = (int)(p.total_rows - row_base);
-    rows_r = s * p.group;
-    const int nt = (rows_r + kRowsWg - 1) / kRowsWg;
-    if (tile < nt) break;
-    tile -= nt;
-    row_base += s;
+  int r = p.num_reqs, row_base = 0, rows_r = 0;
+  if constexpr (kCasc) {
+    // the cascade's groups, one after the other (the fused kernel also holds
+    // the decode waves, and the search below costs it registers)
+    r = 0;
+    for (; r < p.num_reqs; ++r) {
+      int s = p.group_starts[r + 1] - p.group_starts[r];
+      s = s < 0 ? 0 : s;
+      if (row_base + s > p.total_rows) s = (int)(p.total_rows - row_base);
+      rows_r = s * p.group;
+      const int nt = (rows_r + kRowsWg - 1) / kRowsWg;
+      if (tile < nt) break;
+      tile -= nt;
+      row_base += s;
+    }
+  } else {
+    // which request this tile belongs to: 64 requests at a time, one per
+    // lane, with prefix sums of their (clamped) row counts and tile counts
+    // across the wave; the first request whose tile range holds `tile` wins.
+    // One round trip instead of one dependent load per earlier request.
+    const int ln = (int)(threadIdx.x % 64);
+    int64_t rows_before = 0;  // rows of the requests before this batch (at most total_rows)
+    int tiles_before = 0;
+    for (int r0 = 0; r0 < p.num_reqs; r0 += 64) {
+      const int rr = r0 + ln;
+      int s = 0;
+      if (rr < p.num_reqs) s = p.suffix_lens[rr];
+      s = s < 0 ? 0 : s;
+      int incl = s;  // inclusive prefix sum of s over the lanes
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (ln >= off) incl += t;
+      }
+      // the running row count is cut at total_rows, so each request keeps
+      // what is left of it
+      const int64_t rb = min(rows_before + (int64_t)(incl - s), p.total_rows);
+      const int64_t re = min(rows_before + (int64_t)incl, p.total_rows);
+      const int rows = (int)(re - rb) * p.group;
+      const int nt = (rows + kRowsWg - 1) / kRowsWg;
+      int tincl = nt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(tincl, off);
+        if (ln >= off) tincl += t;
+      }
+      const int t0 = tiles_before + tincl - nt;
+      const uint64_t hit = __ballot(rr < p.num_reqs && tile >= t0 && tile < t0 + nt);
+      if (hit) {
+        const int L = __builtin_ctzll(hit);
+        r = r0 + L;
+        row_base = (int)__builtin_amdgcn_readlane((int)rb, L);
+        rows_r = __builtin_amdgcn_readlane(rows, L);
+        tile -= __builtin_amdgcn_readlane(t0, L);
+        break;
+      }
+      rows_before = min(rows_before + (int64_t)__builtin_amdgcn_readlane(incl, 63), p.total_rows);
+      tiles_before += __builtin_amdgcn_readlane(tincl, 63);
+    }
   }
   if (r >= p.num_reqs) return true;
   const int S = rows_r / p.group;

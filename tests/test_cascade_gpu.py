@@ -101,6 +101,21 @@ def test_cascade_many_groups():
     assert report("cascade 60 groups", got, ref, torch.float16, TOL[torch.float16]) <= 1.0
 
 
+def test_cascade_more_groups_than_a_wave():
+    """70 groups: the shared part's work-groups find their group among
+    batches of 64."""
+    rng = np.random.default_rng(660)
+    groups = []
+    for _ in range(70):
+        shared = int(rng.integers(0, 6)) * 16
+        lens = [int(x) for x in rng.integers(1, 150, int(rng.integers(1, 4)))]
+        groups.append((lens, shared))
+    case = workloads.make_grouped_decode_case(660, groups, 8, 2, 128, 16, torch.bfloat16)
+    got = np64(run_cascade(case))
+    ref = oracle_decode(case)
+    assert report("cascade 70 groups", got, ref, torch.bfloat16, TOL[torch.bfloat16]) <= 1.0
+
+
 def test_cascade_long_shared_short_private():
     """One group of 300 sequences on a 2,000-token prefix with 1-40 tokens of
     their own: the shared part dominates the launch. Checked on every sequence

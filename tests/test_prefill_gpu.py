@@ -30,6 +30,20 @@ def test_prefill_group_sizes(hq, hkv):
     assert report("group", np64(run.out), oracle_prefill(case), torch.bfloat16, TOL[torch.bfloat16]) <= 1.0
 
 
+def test_prefill_many_requests():
+    """150 requests (some with empty suffixes, one with a suffix of 80 rows
+    that spans two work-groups at G=4): each work-group finds its request
+    among batches of 64, so the third batch is reached."""
+    rng = np.random.default_rng(604)
+    prefix = [int(x) for x in rng.integers(0, 120, 150)]
+    suffix = [int(x) for x in rng.integers(0, 12, 150)]
+    suffix[140] = 80
+    case = workloads.make_prefill_case(604, prefix, suffix, 8, 2, 64, 16, torch.float16)
+    print(f"prefill 150 requests, {sum(suffix)} rows", flush=True)
+    run = gpu_prefill(case)
+    assert report("150 requests", np64(run.out), oracle_prefill(case), torch.float16, TOL[torch.float16]) <= 1.0
+
+
 def test_prefill_what_day_is_it_shape():
     # 4 cached tokens, 1 new token: the new row equals a decode of 5 tokens
     case = workloads.make_prefill_case(601, [4], [1], 32, 8, 128, 16, torch.bfloat16)
