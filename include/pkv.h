@@ -31,6 +31,11 @@
  *    cut to the capacity, a negative length counts as 0, and a slot outside
  *    [0, num_blocks*B) is skipped. Results for such inputs are unspecified but
  *    every memory access stays inside the caller's buffers.
+ *  - block_tables hold at most 2^24 entries per row (a capacity of at most
+ *    2^29 tokens), so that every position the kernels form fits in 32 bits.
+ *  - scale is the softmax scale of [C] §1 (1/sqrt(d) in the usual model). Any
+ *    finite value is accepted, including negative ones and 0 (uniform weights
+ *    over the visible keys); scale * k_scale * log2(e) must be finite.
  *  - Thread safety: no global mutable state other than the thread-local error
  *    string; concurrent calls on different streams are safe.
  *
@@ -57,7 +62,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 3
+#define PKV_ABI_VERSION 4
 
 typedef enum {
   PKV_F32 = 0,
@@ -194,15 +199,16 @@ int pkv_decode_step_attn(const pkv_tensor* q, const pkv_tensor* k_new, const pkv
  * prefix and the suffix causally. The suffix K, V must already be in the cache
  * (pkv_append them first).
  *
- *  q_suffix      [sum_r S_r, H_q, d] packed request by request; f16/bf16
- *                (or f32 with an f32 cache); rows 16-byte aligned.
+ *  q_suffix      [sum_r S_r, H_q, d] packed request by request; f16 or bf16
+ *                (the products run on matrix cores); rows 16-byte aligned.
  *  k_cache,      caches in the layout above.
  *  v_cache
  *  block_tables  [R, max_blocks] int32; request r reads entries
  *                0 .. ceil((P_r + S_r) / B) - 1.
- *  prefix_lens   [R] int32, P_r >= 0.
+ *  prefix_lens   [R] int32, P_r >= 0 (cut to the table's capacity).
  *  suffix_lens   [R] int32, S_r >= 0; sum_r S_r must equal q_suffix.shape[0]
  *                (the device values are trusted only up to that total).
+ *                sum_r S_r * (H_q / H_kv) must stay below 2^30.
  *  scale,        as for pkv_decode_attn.
  *  k_scale,
  *  v_scale

@@ -132,9 +132,20 @@ int check_block_tables(const pkv_tensor* t, int64_t rows) {
   if (t->dtype != PKV_I32) return fail(PKV_ERR_DTYPE, "block_tables must be int32");
   if (t->shape[0] != rows) return fail(PKV_ERR_SHAPE, "block_tables has %lld rows, expected %lld", (long long)t->shape[0], (long long)rows);
   if (t->shape[1] < 1) return fail(PKV_ERR_SHAPE, "block_tables needs at least one column");
-  if (t->shape[1] > INT32_MAX / 32) return fail(PKV_ERR_SHAPE, "block_tables too wide");
+  // max_blocks * B <= 2^29: with at most 2^30 rows, every position sum the
+  // kernels form (prefix + suffix) stays inside int
+  if (t->shape[1] > ((int64_t)1 << 24)) return fail(PKV_ERR_SHAPE, "block_tables too wide (at most 2^24 blocks per row)");
   if ((t->shape[1] > 1 && t->stride[1] != 1) || (rows > 1 && t->stride[0] < t->shape[1]))
     return fail(PKV_ERR_LAYOUT, "block_tables rows must be contiguous");
+  return PKV_OK;
+}
+
+// The decode walks every 32-token chunk of every sequence with 32-bit chunk
+// indices; with the device lengths cut to the tables' capacity, the most
+// chunks a batch can hold must fit.
+int check_chunk_count(int64_t num_seqs, int64_t max_blocks, int32_t block) {
+  if (num_seqs * ((max_blocks * block + 31) / 32) > INT32_MAX)
+    return fail(PKV_ERR_SHAPE, "num_seqs x table capacity exceeds 2^31 32-token chunks");
   return PKV_OK;
 }
 
@@ -152,6 +163,26 @@ int device_cus() {
 }
 
 pkv::DT to_dt(int d) { return static_cast<pkv::DT>(d); }
+
+// The score multiplier of the kernels, scale * k_scale * log2(e) (k_scale = 1
+// for 16- and 32-bit caches). It must be finite.
+int score_scale(float scale, bool fp8, float k_scale, float* qk) {
+  if (!std::isfinite(scale)) return fail(PKV_ERR_SHAPE, "scale must be finite");
+  *qk = scale * (fp8 ? k_scale : 1.0f) * pkv::kLog2eHost;
+  if (!std::isfinite(*qk)) return fail(PKV_ERR_SHAPE, "scale * k_scale * log2(e) overflows float");
+  return PKV_OK;
+}
+
+// The matrix-core kernels (suffix prefill, the cascade's shared part) take
+// the row maximum of the raw scores and scale it afterwards, which needs a
+// positive multiplier: a negative one is applied by negating q (exact), a
+// zero one by zeroing q (every score 0, uniform weights), as softmax(scale *
+// q K^T) asks for any finite scale.
+void fold_scale(float qk, float* c2, int32_t* q_mode) {
+  if (qk > 0.f) { *c2 = qk; *q_mode = 0; }
+  else if (qk < 0.f) { *c2 = -qk; *q_mode = 1; }
+  else { *c2 = pkv::kLog2eHost; *q_mode = 2; }
+}
 
 // Workspace: partial results [waves_per_head + S][Hq][D + 2] floats, then
 // [S][2] ints of per-sequence partition info.
@@ -242,12 +273,14 @@ int pkv_cascade_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, cons
   }
   if ((rc = check_block_tables(block_tables, S))) return rc;
   if ((rc = check_int_vector(context_lens, "context_lens", S))) return rc;
+  if ((rc = check_chunk_count(S, block_tables->shape[1], cg.block))) return rc;
   if ((rc = check_int_vector(shared_lens, "shared_lens", S))) return rc;
   if ((rc = check_tensor(group_starts, "group_starts", 1))) return rc;
   const int64_t G = group_starts->shape[0] - 1;
   if (G < 0) return fail(PKV_ERR_SHAPE, "group_starts needs at least one entry");
   if ((rc = check_int_vector(group_starts, "group_starts", G + 1))) return rc;
-  if (!std::isfinite(scale)) return fail(PKV_ERR_SHAPE, "scale must be finite");
+  float qk = 0.f;
+  if ((rc = score_scale(scale, fp8, k_scale, &qk))) return rc;
   if (S == 0) return ok();
   if ((rc = check_rows(q, "q"))) return rc;
   if ((rc = check_rows(out, "out"))) return rc;
@@ -262,7 +295,6 @@ int pkv_cascade_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, cons
   if (!aligned16(workspace)) return fail(PKV_ERR_LAYOUT, "workspace must be 16-byte aligned");
   float* sh_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + sh_off);
   float* sh_ml = sh_o + (size_t)splits * S * hq * cg.dim;
-  const float qk = scale * (fp8 ? k_scale : 1.0f) * pkv::kLog2eHost;
 
   // the shared part: every group's queries over its shared prefix, once per
   // row tile (matrix cores)
@@ -283,7 +315,7 @@ int pkv_cascade_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, cons
     if (tiles * cg.hkv > INT32_MAX / 2) return fail(PKV_ERR_SHAPE, "problem too large for one launch");
     sp.tiles_per_head = (int32_t)tiles;
     sp.key_splits = splits;
-    sp.qk_scale_log2 = qk;
+    fold_scale(qk, &sp.qk_scale_log2, &sp.q_mode);
     sp.v_scale = fp8 ? v_scale : 1.0f;
     sp.group_starts = reinterpret_cast<const int32_t*>(group_starts->data);
     sp.context_lens = reinterpret_cast<const int32_t*>(context_lens->data);
@@ -391,12 +423,15 @@ size_t pkv_decode_workspace_bytes(int64_t num_seqs, int32_t num_q_heads, int32_t
 
 }  // extern "C"
 
-namespace {
-// pkv_decode_attn, and with k_new / v_new (both or neither) pkv_decode_step_attn
+namespace pkv {
+// pkv_decode_attn, and with k_new / v_new (both or neither) pkv_decode_step_attn.
+// With `scratch` set, the workspace arguments are ignored: once every argument
+// is valid, scratch(need, &ptr) supplies a workspace of the `need` bytes the
+// launch uses, or returns a status (having set the error message).
 int decode_call(const pkv_tensor* q, const pkv_tensor* k_new, const pkv_tensor* v_new, const pkv_tensor* k_cache,
                 const pkv_tensor* v_cache, const pkv_tensor* block_tables, const pkv_tensor* context_lens,
                 float scale, float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
-                const pkv_tensor* out, void* stream) {
+                ScratchFn scratch, const pkv_tensor* out, void* stream) {
   int rc;
   CacheGeom cg;
   if ((rc = check_caches(k_cache, v_cache, &cg))) return rc;
@@ -419,7 +454,9 @@ int decode_call(const pkv_tensor* q, const pkv_tensor* k_new, const pkv_tensor* 
   }
   if ((rc = check_block_tables(block_tables, S))) return rc;
   if ((rc = check_int_vector(context_lens, "context_lens", S))) return rc;
-  if (!std::isfinite(scale)) return fail(PKV_ERR_SHAPE, "scale must be finite");
+  if ((rc = check_chunk_count(S, block_tables->shape[1], cg.block))) return rc;
+  float qk = 0.f;
+  if ((rc = score_scale(scale, fp8, k_scale, &qk))) return rc;
   const bool step = k_new != nullptr || v_new != nullptr;
   if (step) {
     if ((rc = check_tensor(k_new, "k_new", 3))) return rc;
@@ -443,6 +480,10 @@ int decode_call(const pkv_tensor* q, const pkv_tensor* k_new, const pkv_tensor* 
 
   pkv::DecodePlan plan;
   const size_t need = decode_ws_bytes(S, (int32_t)hq, cg.hkv, cg.dim, &plan);
+  if (scratch) {
+    if ((rc = scratch(need, &workspace))) return rc;
+    workspace_bytes = need;
+  }
   if (workspace == nullptr || workspace_bytes < need)
     return fail(PKV_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need, workspace_bytes);
   if (!aligned16(workspace)) return fail(PKV_ERR_LAYOUT, "workspace must be 16-byte aligned");
@@ -462,7 +503,7 @@ int decode_call(const pkv_tensor* q, const pkv_tensor* k_new, const pkv_tensor* 
   p.ws_o = reinterpret_cast<float*>(workspace);
   p.ws_ml = p.ws_o + slots * hq * cg.dim;
   p.seq_info = reinterpret_cast<int32_t*>(p.ws_ml + slots * hq * 2);
-  p.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * pkv::kLog2eHost;
+  p.qk_scale_log2 = qk;  // the decode scales before its maximum: any sign works
   p.v_scale = fp8 ? v_scale : 1.0f;
   if (step) {
     p.k_new = k_new->data; p.kn_s0 = k_new->stride[0]; p.kn_s1 = k_new->stride[1];
@@ -474,7 +515,7 @@ int decode_call(const pkv_tensor* q, const pkv_tensor* k_new, const pkv_tensor* 
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return ok();
 }
-}  // namespace
+}  // namespace pkv
 
 extern "C" {
 
@@ -482,8 +523,8 @@ int pkv_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_te
                     const pkv_tensor* block_tables, const pkv_tensor* context_lens, float scale,
                     float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
                     const pkv_tensor* out, void* stream) {
-  return decode_call(q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
-                     workspace, workspace_bytes, out, stream);
+  return pkv::decode_call(q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
+                          v_scale, workspace, workspace_bytes, nullptr, out, stream);
 }
 
 int pkv_decode_step_attn(const pkv_tensor* q, const pkv_tensor* k_new, const pkv_tensor* v_new,
@@ -492,8 +533,8 @@ int pkv_decode_step_attn(const pkv_tensor* q, const pkv_tensor* k_new, const pkv
                          size_t workspace_bytes, const pkv_tensor* out, void* stream) {
   if (!k_new) return fail(PKV_ERR_NULL, "k_new: descriptor is NULL");
   if (!v_new) return fail(PKV_ERR_NULL, "v_new: descriptor is NULL");
-  return decode_call(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
-                     workspace, workspace_bytes, out, stream);
+  return pkv::decode_call(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
+                          workspace, workspace_bytes, nullptr, out, stream);
 }
 
 int pkv_suffix_prefill_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_tensor* v_cache,
@@ -524,7 +565,8 @@ int pkv_suffix_prefill_attn(const pkv_tensor* q, const pkv_tensor* k_cache, cons
   if ((rc = check_int_vector(prefix_lens, "prefix_lens", R))) return rc;
   if ((rc = check_int_vector(suffix_lens, "suffix_lens", R))) return rc;
   if ((rc = check_block_tables(block_tables, R))) return rc;
-  if (!std::isfinite(scale)) return fail(PKV_ERR_SHAPE, "scale must be finite");
+  float qk = 0.f;
+  if ((rc = score_scale(scale, fp8, k_scale, &qk))) return rc;
   if (total == 0 || R == 0) return ok();
   if ((rc = check_rows(q, "q_suffix"))) return rc;
   if ((rc = check_rows(out, "out"))) return rc;
@@ -545,7 +587,7 @@ int pkv_suffix_prefill_attn(const pkv_tensor* q, const pkv_tensor* k_cache, cons
   const int64_t tiles = (total * p.group + W - 1) / W + R;
   if (tiles * cg.hkv > INT32_MAX) return fail(PKV_ERR_SHAPE, "problem too large for one launch");
   p.tiles_per_head = (int32_t)tiles;
-  p.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * pkv::kLog2eHost;
+  fold_scale(qk, &p.qk_scale_log2, &p.q_mode);
   p.v_scale = fp8 ? v_scale : 1.0f;
   hipError_t e = pkv::launch_prefill(p, to_dt(q->dtype), to_dt(cg.dtype), cg.dim, cg.block, (hipStream_t)stream);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pkv.h"
+
 namespace pkv {
 
 constexpr float kLog2eHost = 1.4426950408889634f;
@@ -66,8 +68,9 @@ struct PrefillParams {
   int32_t num_reqs, hq, hkv, group, num_blocks;
   int64_t total_rows;                 // sum_r S_r (host-known)
   int32_t tiles_per_head;             // grid size / hkv (upper bound on tiles)
-  float qk_scale_log2;
+  float qk_scale_log2;                // |softmax scale * k_scale| * log2(e), > 0
   float v_scale;
+  int32_t q_mode;                     // 0: q as given; 1: q negated (negative scale); 2: q zeroed (zero scale)
   // cascade decode's shared part (group_starts == nullptr otherwise): the
   // "requests" are groups of sequences group_starts[g] .. group_starts[g+1]-1,
   // one query row per (sequence, head), attending to the group's shared
@@ -90,6 +93,19 @@ __host__ __device__ inline int cascade_chunk(int L, int splits) {
   const int c = (L + splits - 1) / splits;
   return (c + kCascadeChunkAlign - 1) / kCascadeChunkAlign * kCascadeChunkAlign;
 }
+
+// Supplies a decode workspace of `need` bytes in place of the caller's (the
+// entry point that allocates nothing); returns a pkv_status.
+typedef int (*ScratchFn)(size_t need, void** ptr);
+
+// Validation and launch of pkv_decode_attn (k_new = v_new = nullptr) and
+// pkv_decode_step_attn; with `scratch` set, the workspace arguments are
+// ignored and scratch(need, &ptr) supplies the workspace once every argument
+// is valid.
+int decode_call(const pkv_tensor* q, const pkv_tensor* k_new, const pkv_tensor* v_new, const pkv_tensor* k_cache,
+                const pkv_tensor* v_cache, const pkv_tensor* block_tables, const pkv_tensor* context_lens,
+                float scale, float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                ScratchFn scratch, const pkv_tensor* out, void* stream);
 
 // Decode launch plan shared by the launcher and the workspace-size query.
 struct DecodePlan { int32_t waves_per_head; int32_t total_waves; };

@@ -60,8 +60,22 @@ __device__ __forceinline__ const char* uniform_ptr(const void* base, int64_t off
 // wait insertion would otherwise drain every direct load in flight before each
 // LDS read, because it cannot tell which buffer a load writes. The kernel
 // orders these loads itself with explicit waits before its barriers.
+// The LDS destination travels in m0, a register the compiler reserves: the
+// block saves m0 and restores it after the load has been issued (the load
+// reads m0 at issue), so whatever the compiler keeps there survives. On the
+// GFX9 family a load that takes its LDS address from m0 must not directly
+// follow the scalar write of m0: one wait state (s_nop 0) separates them.
 __device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(lds), "v"(voff), "s"(base) : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(base)
+      : "memory");
 }
 // Work-group barrier that is also a compiler memory barrier: no LDS (or
 // other memory) access is moved across it, in either direction. Its wait is
@@ -73,7 +87,8 @@ __device__ __forceinline__ uint32_t lds_address(const char* p) {
 }
 
 // kFast: a bf16 cache's values are converted to f16 in LDS (exact for
-// |v| < 65520, and f16 P carries 11 bits, as with an f16 cache); a work-group
+// 2^-17 <= |v| < 65520; smaller values land in f16's subnormal range, within
+// 2^-25 absolute; f16 P carries 11 bits, as with an f16 cache); a work-group
 // that meets a larger or non-finite value redoes its rows without it.
 template <typename TQ, typename TC, bool kFast>
 struct Types {
@@ -285,19 +300,21 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     int tiles_before = 0;
     for (int r0 = 0; r0 < p.num_reqs; r0 += 64) {
       const int rr = r0 + ln;
-      int s = 0;
+      // device lengths are not trusted: each is cut to [0, total_rows] and
+      // summed in 64 bits, so no sum can wrap
+      int64_t s = 0;
       if (rr < p.num_reqs) s = p.suffix_lens[rr];
-      s = s < 0 ? 0 : s;
-      int incl = s;  // inclusive prefix sum of s over the lanes
+      s = s < 0 ? 0 : (s > p.total_rows ? p.total_rows : s);
+      int64_t incl = s;  // inclusive prefix sum of s over the lanes
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(incl, off);
+        const int64_t t = __shfl_up(incl, off);
         if (ln >= off) incl += t;
       }
       // the running row count is cut at total_rows, so each request keeps
       // what is left of it
-      const int64_t rb = min(rows_before + (int64_t)(incl - s), p.total_rows);
-      const int64_t re = min(rows_before + (int64_t)incl, p.total_rows);
+      const int64_t rb = min(rows_before + (incl - s), p.total_rows);
+      const int64_t re = min(rows_before + incl, p.total_rows);
       const int rows = (int)(re - rb) * p.group;
       const int nt = (rows + kRowsWg - 1) / kRowsWg;
       int tincl = nt;
@@ -316,7 +333,7 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
         tile -= __builtin_amdgcn_readlane(t0, L);
         break;
       }
-      rows_before = min(rows_before + (int64_t)__builtin_amdgcn_readlane(incl, 63), p.total_rows);
+      rows_before = min(rows_before + __shfl(incl, 63), p.total_rows);
       tiles_before += __builtin_amdgcn_readlane(tincl, 63);
     }
   }
@@ -334,8 +351,11 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     kv_len = max(min(P - k0, chunk), 0);
     bt = p.block_tables + (int64_t)row_base * p.bt_s0 + (kv_len > 0 ? k0 / BLK : 0);
   } else {
+    // the prefix is cut to the table's capacity before the suffix is added:
+    // cap <= 2^29 and S <= 2^30 (both checked on the host), so P + S and
+    // every P + i below stay inside int
     P = p.prefix_lens[r];
-    P = P < 0 ? 0 : P;
+    P = P < 0 ? 0 : (P > cap ? cap : P);
     kv_len = P + S;
     if (kv_len > cap) kv_len = cap;
     bt = p.block_tables + (int64_t)r * p.bt_s0;
@@ -382,6 +402,18 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     F v = {};
     if (rvalid) v = load_frag8(qrow + 16 * c + 8 * h0);
     qf[c] = v;
+  }
+  // the kernel's score scale c2 is positive: a negative softmax scale is
+  // applied by negating q (exact), a zero one by zeroing it (every score 0)
+  if (p.q_mode != 0) {
+    const uint32_t keep = p.q_mode == 1 ? ~0u : 0u;
+#pragma unroll
+    for (int c = 0; c < QS; ++c) {
+      u32x4 w = __builtin_bit_cast(u32x4, qf[c]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (w[e] & keep) ^ (keep & 0x80008000u);
+      qf[c] = __builtin_bit_cast(F, w);
+    }
   }
   const int lim = casc ? ctx_row - 1 : P + tok;  // last key position this row may see
   const float c2 = p.qk_scale_log2;
@@ -514,7 +546,7 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
     {  // the other 16 keys of this row sit in lane l ^ 32
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c2;  // scale > 0: max commutes
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c2;  // c2 > 0: max commutes
     }
     const bool grow = mx > m_run + kLazy;
     const bool any = __any(grow);
@@ -702,12 +734,15 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
 
   // step j (every branch is uniform over the wave): PV(j) with pcur,
   // P(j+1) = softmax(S(j+1)) into pnext, S(j+2) = QK(j+2)
+  // The exact pass (bf16 P as hi + lo) holds twice the P registers; it reads
+  // its K operands only after the value products, so that it fits in the
+  // registers without spilling (it is rare: its speed does not matter).
   auto step = [&](int j, int bk, int bv, int t, const PFrag<FV>& pcur, PFrag<FV>& pnext) {
     const bool do_pv = j < nsub, do_sm = j + 1 < nsub, do_qk = j + 2 < nsub;
     VOps vo;
     KOps ko;
     if (do_pv) load_v(bv, t, vo);
-    if (do_qk) load_k(bk, t, ko);
+    if (!T::kSplitP && do_qk) load_k(bk, t, ko);
     float alpha = 1.f;
     bool rescale = false;
     if (do_sm) rescale = softmax(sc, 32 * (j + 1), 32 * (j + 2) > full_keys_w, pnext, alpha);
@@ -719,6 +754,7 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
 #pragma unroll
       for (int n = 0; n < NT; ++n) acc[n] *= alpha;
     }
+    if (T::kSplitP && do_qk) load_k(bk, t, ko);
     if (do_qk) sc = qk(ko);
   };
   // A step away from the edges (no mask, no tail, every product present).
@@ -766,7 +802,7 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
       __builtin_amdgcn_sched_barrier(0);
       {  // the other 16 keys of this row sit in lane l ^ 32
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c2;  // scale > 0: max commutes
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c2;  // c2 > 0: max commutes
       }
       const bool grow = mx > m_run + kLazy;
       const bool rescale = __any(grow);

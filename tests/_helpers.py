@@ -6,9 +6,12 @@ from __future__ import annotations
 import math
 from dataclasses import dataclass
 
+import os
+
 import numpy as np
 import torch
 
+import _margins
 import oracle
 import prefix_reuse_amd as pkv
 import workloads
@@ -39,7 +42,7 @@ def half_ulp(x: np.ndarray, dtype: torch.dtype) -> np.ndarray:
     return 0.5 * np.exp2(np.floor(np.log2(a)) - m)
 
 
-def report(name: str, got: np.ndarray, ref: np.ndarray, out_dtype=None, tol=None) -> float:
+def report(name: str, got: np.ndarray, ref: np.ndarray, out_dtype=None, tol=None, record: bool = True) -> float:
     """Print the worst error and return it as a multiple of the allowed error.
 
     Allowed error per element = tol + half an ulp of the output dtype at |ref|:
@@ -58,8 +61,14 @@ def report(name: str, got: np.ndarray, ref: np.ndarray, out_dtype=None, tol=None
     allowed = tol + half_ulp(ref, out_dtype)
     ratio = float(np.nanmax(err / allowed))
     bad = int(np.sum(~(err <= allowed)))
+    if bad:  # a NaN or inf where the oracle is finite counts as a violation, not as a skipped element
+        ratio = max(ratio, float("inf") if np.any(~np.isfinite(err)) else ratio)
     print(msg + f" worst err/allowed={ratio:.3f} (tol {tol:g} + half-ulp of {out_dtype}), violations={bad}",
           flush=True)
+    test = os.environ.get("PYTEST_CURRENT_TEST", "")
+    family = test.split(" ")[0].split("[")[0].replace("tests/", "") or name
+    if record:
+        _margins.record(family, name, ratio, worst, float(np.nanmax(np.abs(ref))))
     return ratio
 
 

@@ -22,3 +22,18 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Worst err/allowed of every parity family that ran (1.0 = at the gate)."""
+    try:
+        import _margins
+    except ImportError:  # pragma: no cover
+        return
+    if not _margins.WORST:
+        return
+    tr = terminalreporter
+    tr.write_sep("-", "parity margins: worst err/allowed per test family (gate = 1.0)")
+    for fam in sorted(_margins.WORST):
+        ratio, case, err, ref = _margins.WORST[fam]
+        tr.write_line(f"{ratio:7.3f}  {fam}  (case {case}: max|err| {err:.2e}, max|ref| {ref:.2e})")

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert pkv.abi_version() == 3
+    assert pkv.abi_version() == 4
 
 
 def T(shape, dtype, strides=None, ptr=FAKE):
@@ -167,6 +167,27 @@ def test_prefill_rejects_bad_arguments():
     assert f(R(q), R(kc), R(vc), R(ok_bt), R(pl), R(T([3], I32)), 0.1, 1.0, 1.0, R(q), None) == 3
     assert f(R(q), R(kc), R(vc), R(T([2, 4], I32)), R(pl), R(sl), 0.1, 1.0, 1.0, R(T([9, 4, 64], F16)), None) == 3
     assert f(R(q), R(kc), R(vc), R(ok_bt), R(pl), R(sl), float("nan"), 1.0, 1.0, R(q), None) == 3
+
+
+def test_scale_and_table_limits_are_checked():
+    """scale * k_scale * log2(e) must be finite; block tables hold at most 2^24
+    entries per row (so every position fits in 32 bits); a batch must hold
+    fewer than 2^31 32-token chunks."""
+    kc, vc = caches()
+    args = (T([2, 4, 64], F16), kc, vc, T([2, 4], I32), T([2], I32), T([2, 4, 64], F16))
+    assert decode(*args, scale=float("inf")) == 3 and "finite" in err()
+    k8, v8 = caches(dt=FP8)
+    assert decode(T([2, 4, 64], F16), k8, v8, T([2, 4], I32), T([2], I32), T([2, 4, 64], F16), scale=3e38,
+                  ks=10.0) == 3 and "overflows" in err()
+    wide = T([2, 2 ** 24 + 1], I32)
+    assert decode(T([2, 4, 64], F16), kc, vc, wide, T([2], I32), T([2, 4, 64], F16)) == 3 and "wide" in err()
+    many = 2 ** 14
+    rc = decode(T([many, 4, 64], F16), kc, vc, T([many, 2 ** 24], I32), T([many], I32), T([many, 4, 64], F16))
+    assert rc == 3 and "chunks" in err()
+    f = pkv.lib.pkv_suffix_prefill_attn
+    q = T([10, 4, 64], F16)
+    assert f(R(q), R(kc), R(vc), R(T([2, 2 ** 24 + 1], I32)), R(T([2], I32)), R(T([2], I32)), 0.1, 1.0, 1.0,
+             R(q), None) == 3
 
 
 def test_empty_batches_are_accepted_without_launch():

@@ -24,7 +24,14 @@ SAMPLE_SEQS = (0, 7)
 SAMPLE_KV_HEADS = (0, 7)
 
 
-def _layer_on_gpu(case: workloads.LongContextFp8Case, layer: int, dev):
+def _rows(case, layer, s, dev, which, v_mean):
+    x = case.raw_kv(layer, s, dev, which)
+    if which == "v" and v_mean is not None:
+        x = x + v_mean.to(dev)
+    return x
+
+
+def _layer_on_gpu(case: workloads.LongContextFp8Case, layer: int, dev, q_mult=1.0, v_mean=None):
     n = case.context_len
     kc, vc = pkv.empty_caches(case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim,
                               torch.float8_e4m3fn, dev)
@@ -34,13 +41,13 @@ def _layer_on_gpu(case: workloads.LongContextFp8Case, layer: int, dev):
     amax = {"k": 0.0, "v": 0.0}
     for s in range(case.num_seqs):
         for w in amax:
-            amax[w] = max(amax[w], float(case.raw_kv(layer, s, dev, w).abs().max().item()))
+            amax[w] = max(amax[w], float(_rows(case, layer, s, dev, w, v_mean).abs().max().item()))
     k_scale = float(np.float32(amax["k"]) / np.float32(448.0))
     v_scale = float(np.float32(amax["v"]) / np.float32(448.0))
     for s in range(case.num_seqs):
-        pkv.append(case.raw_kv(layer, s, dev, "k"), case.raw_kv(layer, s, dev, "v"),
+        pkv.append(_rows(case, layer, s, dev, "k", v_mean), _rows(case, layer, s, dev, "v", v_mean),
                    case.slots(s, 0, n).to(dev), kc, vc, k_scale, v_scale)
-    q = case.raw_q(layer, dev)
+    q = (case.raw_q(layer, dev).float() * q_mult).to(torch.bfloat16)  # q_mult a power of two: exact
     out = pkv.decode_attn(q, kc, vc, case.block_tables.to(dev),
                           torch.full((case.num_seqs,), n, dtype=torch.int32, device=dev), case.scale,
                           k_scale=k_scale, v_scale=v_scale)
@@ -48,14 +55,29 @@ def _layer_on_gpu(case: workloads.LongContextFp8Case, layer: int, dev):
     return kc, vc, q, out, k_scale, v_scale
 
 
-@pytest.mark.parametrize("layer", [0, 31])
-def test_config5_long_context_fp8_sampled(layer):
+def stress_v_mean(case, seed=5):
+    """Per-(KV head, dim) mean in [0.5, 2] with a random sign, added to every
+    V row of the stress layer: outputs are then of order 1."""
+    g = torch.Generator().manual_seed(seed)
+    h, d = case.num_kv_heads, case.head_dim
+    return (0.5 + 1.5 * torch.rand(h, d, generator=g)) * torch.where(torch.rand(h, d, generator=g) < 0.5, -1.0, 1.0)
+
+
+@pytest.mark.parametrize("layer,stress", [(0, False), (31, False), (7, True)])
+def test_config5_long_context_fp8_sampled(layer, stress):
+    """stress=True: the same full-size layer with q scaled by 8 (a sharp
+    softmax over 100,000 keys) and V given a per-dimension mean, so that the
+    outputs are of order 1 and the 2e-2 gate can fail (with N(0,1) data at
+    100k keys max|out| is ~0.02, below the gate); an all-zero output must
+    fail it."""
     dev = torch.device("cuda")
     case = workloads.config5_long_context_fp8()
     n, bsz, d = case.context_len, case.block_size, case.head_dim
     group = case.num_q_heads // case.num_kv_heads
-    print(f"config5 layer {layer}: {case.num_seqs} x {n} tokens, fp8, B={bsz}", flush=True)
-    kc, vc, q, out, k_scale, v_scale = _layer_on_gpu(case, layer, dev)
+    v_mean = stress_v_mean(case) if stress else None
+    print(f"config5 layer {layer}{' (stress: q x8, V + mean)' if stress else ''}: {case.num_seqs} x {n} tokens, "
+          f"fp8, B={bsz}", flush=True)
+    kc, vc, q, out, k_scale, v_scale = _layer_on_gpu(case, layer, dev, 8.0 if stress else 1.0, v_mean)
     assert torch.isfinite(out.float()).all()
     q_host = q.float().cpu().double().numpy()
     out_host = out.float().cpu().double().numpy()
@@ -67,7 +89,7 @@ def test_config5_long_context_fp8_sampled(layer):
         for h in SAMPLE_KV_HEADS:
             # expected codes of this (sequence, KV head), from the raw rows
             raw_k = case.raw_kv(layer, s, dev, "k")[:, h].cpu().numpy()
-            raw_v = case.raw_kv(layer, s, dev, "v")[:, h].cpu().numpy()
+            raw_v = _rows(case, layer, s, dev, "v", v_mean)[:, h].cpu().numpy()
             ek = oracle.e4m3fn_quantize(raw_k, k_scale)                   # [n, d]
             ev = oracle.e4m3fn_quantize(raw_v, v_scale)
             # bytes the GPU stored for this sequence's blocks, in logical order
@@ -85,4 +107,7 @@ def test_config5_long_context_fp8_sampled(layer):
                 ident, np.array([n]), case.scale, fp8=True, k_scale=k_scale, v_scale=v_scale)
             got = out_host[s:s + 1, heads]
             worst = max(worst, report(f"config5 L{layer} s{s} h{h}", got, ref, torch.bfloat16, TOL["fp8"]))
+            if stress:
+                assert np.abs(ref).max() >= 0.5
+                assert report("zeros (must fail)", np.zeros_like(ref), ref, torch.bfloat16, TOL["fp8"], record=False) > 1.0
     assert worst <= 1.0

@@ -98,3 +98,58 @@ def test_config3_shared_prefix_decode_full():
     run = gpu_decode(case)
     ref = oracle_decode(case)
     assert report("config3", np64(run.out), ref, torch.bfloat16, TOL[torch.bfloat16]) <= 1.0
+
+
+def _fp8_decode_vs_oracle(case, q_dtype, name):
+    inp = fp8_inputs_from_pools(case, q_dtype)
+    run = gpu_fp8_decode(case, inp, q_dtype)
+    kc, vc = oracle_fp8_caches(case, inp)
+    ref = oracle.decode_attention(np64(case.q.to(q_dtype)), kc, vc, case.block_tables.numpy(),
+                                  case.context_lens.numpy(), case.scale, fp8=True,
+                                  k_scale=inp.k_scale, v_scale=inp.v_scale)
+    return np64(run.out), ref
+
+
+@pytest.mark.parametrize("waves", [2, 8, 24])
+@pytest.mark.parametrize("q_dtype", [torch.bfloat16, torch.float16])
+def test_decode_fp8_many_chunks_per_wave(waves, q_dtype, monkeypatch):
+    """The long-context path over an fp8 cache: with PKV_DECODE_WAVES forcing
+    few waves, every wave walks many 32-token chunks, crosses sequences and
+    writes partials that the combine merges (2 KV heads: 1, 4 or 12 waves per
+    head over ~430 chunks)."""
+    print(f"fp8 decode, {waves} waves, q {q_dtype}", flush=True)
+    case = workloads.make_decode_case(420, [6000, 129, 2500, 1000, 3, 0, 33, 4100], 8, 2, 128, 32, torch.float32)
+    monkeypatch.setenv("PKV_DECODE_WAVES", str(waves))
+    got, ref = _fp8_decode_vs_oracle(case, q_dtype, "fp8 waves")
+    assert report(f"fp8 waves={waves}", got, ref, q_dtype, TOL["fp8"]) <= 1.0
+
+
+def sharpen(case, q_mult=8.0, seed=0):
+    """A long-context stress input whose outputs are of order 1: q scaled by
+    q_mult (a sharp softmax over few keys) and V given a per-(KV head, dim)
+    mean in [0.5, 2] with a random sign. With plain N(0,1) data an output over
+    n keys has magnitude ~ 1/sqrt(n), so at long contexts an absolute gate
+    could not tell a result from zeros."""
+    g = torch.Generator().manual_seed(seed)
+    h, d = case.num_kv_heads, case.head_dim
+    mu = (0.5 + 1.5 * torch.rand(h, d, generator=g)) * torch.where(torch.rand(h, d, generator=g) < 0.5, -1.0, 1.0)
+    case.q = (case.q.float() * q_mult).to(case.q.dtype)
+    case.v_pool = (case.v_pool.float() + mu).to(case.v_pool.dtype)  # NaN poison stays NaN
+    case.v_new = (case.v_new.float() + mu).to(case.v_new.dtype)
+    return mu
+
+
+@pytest.mark.parametrize("waves", [4, 0])
+def test_decode_fp8_sharp_long_context(waves, monkeypatch):
+    """fp8 cache, 20,000- and 9,000-token contexts with a sharpened q and V
+    carrying a per-dimension mean, so that |out| = O(1) and the 2e-2 gate can
+    fail; with 4 waves in all (2 per KV head) each wave walks ~450 chunks. An
+    all-zero output must fail the same gate."""
+    case = workloads.make_decode_case(421, [20000, 9000], 8, 2, 128, 32, torch.float32)
+    sharpen(case, seed=421)
+    if waves:
+        monkeypatch.setenv("PKV_DECODE_WAVES", str(waves))
+    got, ref = _fp8_decode_vs_oracle(case, torch.bfloat16, "fp8 sharp")
+    assert np.abs(ref).max() >= 0.5
+    assert report(f"fp8 sharp waves={waves}", got, ref, torch.bfloat16, TOL["fp8"]) <= 1.0
+    assert report("zeros (must fail)", np.zeros_like(ref), ref, torch.bfloat16, TOL["fp8"], record=False) > 1.0
