@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 4
+#define PKV_ABI_VERSION 5
 
 typedef enum {
   PKV_F32 = 0,
@@ -162,6 +162,26 @@ int pkv_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_te
                     const pkv_tensor* block_tables, const pkv_tensor* context_lens, float scale,
                     float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
                     const pkv_tensor* out, void* stream);
+
+/*
+ * pkv_decode_attn_noalloc — pkv_decode_attn without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops without an allocator, harnesses that forbid allocation).
+ * Same arguments, results and bits as pkv_decode_attn, minus the workspace:
+ * the partial results live in a device-resident array of 32 MiB inside the
+ * library, one per GPU, set up on the first call on each device and held
+ * until the process ends. The call never allocates or frees memory.
+ *  - A batch whose pkv_decode_workspace_bytes(...) exceeds 32 MiB is rejected
+ *    with PKV_ERR_WORKSPACE before anything is launched (at 8 KV heads,
+ *    d = 128 and 256 compute units: up to ~500 sequences of 32 query heads).
+ *  - Every call on one GPU shares that GPU's array and nothing in it needs
+ *    clearing; calls that overlap on one GPU (different streams, or different
+ *    threads without ordering) race on it and give wrong results. Calls
+ *    ordered on one stream are safe.
+ */
+int pkv_decode_attn_noalloc(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_tensor* v_cache,
+                            const pkv_tensor* block_tables, const pkv_tensor* context_lens, float scale,
+                            float k_scale, float v_scale, const pkv_tensor* out, void* stream);
 
 /*
  * pkv_decode_step_attn — a whole decode step in one call: pkv_append of each

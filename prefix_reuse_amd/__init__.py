@@ -20,7 +20,8 @@ import torch
 
 __all__ = [
     "LIB_PATH", "lib", "PkvError",
-    "append", "decode_attn", "decode_step_attn", "suffix_prefill_attn", "decode_workspace_bytes",
+    "append", "decode_attn", "decode_attn_noalloc", "decode_step_attn", "suffix_prefill_attn",
+    "decode_workspace_bytes",
     "cascade_decode_attn", "cascade_workspace_bytes",
     "empty_caches", "caches_from_logical", "k_logical", "v_logical", "abi_version",
 ]
@@ -64,6 +65,9 @@ def _load() -> ctypes.CDLL:
     L.pkv_decode_attn.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                   ctypes.c_void_p, ctypes.c_size_t, P, ctypes.c_void_p]
     L.pkv_decode_attn.restype = ctypes.c_int
+    L.pkv_decode_attn_noalloc.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float, P,
+                                          ctypes.c_void_p]
+    L.pkv_decode_attn_noalloc.restype = ctypes.c_int
     L.pkv_decode_step_attn.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                        ctypes.c_void_p, ctypes.c_size_t, P, ctypes.c_void_p]
     L.pkv_decode_step_attn.restype = ctypes.c_int
@@ -184,6 +188,22 @@ def decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                              float(k_scale), float(v_scale), ws_ptr, ws_bytes, _ref(do),
                              _stream(q.device))
     _check("pkv_decode_attn", rc)
+    return out
+
+
+def decode_attn_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                        out: Optional[torch.Tensor] = None, k_scale: float = 1.0,
+                        v_scale: float = 1.0) -> torch.Tensor:
+    """pkv_decode_attn without a workspace: the library's device-resident
+    scratch holds the partial results (see include/pkv.h). Pass ``out`` to
+    avoid the one allocation this wrapper would otherwise make."""
+    if out is None:
+        out = torch.empty_like(q)
+    dq, dkc, dvc, dbt, dcl, do = map(_desc, (q, k_cache, v_cache, block_tables, context_lens, out))
+    rc = lib.pkv_decode_attn_noalloc(_ref(dq), _ref(dkc), _ref(dvc), _ref(dbt), _ref(dcl), float(scale),
+                                     float(k_scale), float(v_scale), _ref(do), _stream(q.device))
+    _check("pkv_decode_attn_noalloc", rc)
     return out
 
 

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert pkv.abi_version() == 4
+    assert pkv.abi_version() == 5
 
 
 def T(shape, dtype, strides=None, ptr=FAKE):
@@ -260,3 +260,13 @@ def test_missing_library_fails_loudly(tmp_path):
                          text=True, timeout=120)
     assert res.returncode != 0
     assert "ImportError" in res.stderr and "There is no CPU fallback" in res.stderr
+
+
+def test_noalloc_decode_rejects_a_batch_beyond_its_scratch_before_launch():
+    """pkv_decode_attn_noalloc keeps its partial results in a fixed 32 MiB
+    device array; a batch that needs more is refused on the host."""
+    kc, vc = caches(h=8, d=128)
+    s = 4000
+    rc = pkv.lib.pkv_decode_attn_noalloc(R(T([s, 32, 128], F16)), R(kc), R(vc), R(T([s, 4], I32)), R(T([s], I32)),
+                                         0.1, 1.0, 1.0, R(T([s, 32, 128], F16)), None)
+    assert rc == 6 and "scratch" in err()
