@@ -734,15 +734,12 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
 
   // step j (every branch is uniform over the wave): PV(j) with pcur,
   // P(j+1) = softmax(S(j+1)) into pnext, S(j+2) = QK(j+2)
-  // The exact pass (bf16 P as hi + lo) holds twice the P registers; it reads
-  // its K operands only after the value products, so that it fits in the
-  // registers without spilling (it is rare: its speed does not matter).
   auto step = [&](int j, int bk, int bv, int t, const PFrag<FV>& pcur, PFrag<FV>& pnext) {
     const bool do_pv = j < nsub, do_sm = j + 1 < nsub, do_qk = j + 2 < nsub;
     VOps vo;
     KOps ko;
     if (do_pv) load_v(bv, t, vo);
-    if (!T::kSplitP && do_qk) load_k(bk, t, ko);
+    if (do_qk) load_k(bk, t, ko);
     float alpha = 1.f;
     bool rescale = false;
     if (do_sm) rescale = softmax(sc, 32 * (j + 1), 32 * (j + 2) > full_keys_w, pnext, alpha);
@@ -754,7 +751,6 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
 #pragma unroll
       for (int n = 0; n < NT; ++n) acc[n] *= alpha;
     }
-    if (T::kSplitP && do_qk) load_k(bk, t, ko);
     if (do_qk) sc = qk(ko);
   };
   // A step away from the edges (no mask, no tail, every product present).
