@@ -13,6 +13,7 @@ order ``[num_blocks, B, H_kv, d]``.
 from __future__ import annotations
 
 import ctypes
+import os
 from pathlib import Path
 from typing import Optional, Tuple
 
@@ -26,7 +27,9 @@ __all__ = [
     "empty_caches", "caches_from_logical", "k_logical", "v_logical", "abi_version",
 ]
 
-LIB_PATH = Path(__file__).resolve().parent / "libpkv.so"
+# PKV_LIBRARY selects another build of the same library (the CPU sanitizer
+# build, libpkv_san.so); by default the in-tree libpkv.so is loaded
+LIB_PATH = Path(os.environ.get("PKV_LIBRARY") or Path(__file__).resolve().parent / "libpkv.so")
 
 _DT = {
     torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float8_e4m3fn: 3,

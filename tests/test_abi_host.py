@@ -256,8 +256,11 @@ def test_missing_library_fails_loudly(tmp_path):
     src = Path(pkv.__file__).parent
     for f in src.glob("*.py"):
         shutil.copy(f, pkg / f.name)  # the package without its built library
+    import os
+
+    env = {k: v for k, v in os.environ.items() if k != "PKV_LIBRARY"}
     res = subprocess.run([sys.executable, "-c", "import prefix_reuse_amd"], cwd=tmp_path, capture_output=True,
-                         text=True, timeout=120)
+                         text=True, timeout=120, env=env)
     assert res.returncode != 0
     assert "ImportError" in res.stderr and "There is no CPU fallback" in res.stderr
 
