@@ -637,41 +637,27 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     block_barrier();
   };
 
-  // bf16 -> f16 in place for this thread's share of V stage `st`, tracking
-  // the largest |bf16| bit pattern among live keys (keys >= kv_len hold
-  // whatever the cache slots hold and are zeroed before use)
-  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-  u16x2 vmax = {0, 0};
-  // two bf16 values (one word) -> two f16 values; `live` masks the halves
-  // that count towards the maximum
-  auto conv_word = [&](uint32_t x, uint32_t live) -> uint32_t {
-    vmax = __builtin_elementwise_max(vmax, __builtin_bit_cast(u16x2, x & 0x7fff7fffu & live));
+  // bf16 -> f16 in place for this thread's share of V stage `st` (keys >=
+  // kv_len hold whatever the cache slots hold and are zeroed before use). A
+  // value beyond f16 range becomes inf here; the check after the last stage
+  // finds it in the accumulators.
+  // two bf16 values (one word) -> two f16 values
+  auto conv_word = [&](uint32_t x) -> uint32_t {
     const f16x2 h = {(f16_t)__uint_as_float(x << 16), (f16_t)__uint_as_float(x & 0xffff0000u)};
     return __builtin_bit_cast(uint32_t, h);
   };
   auto convert_v = [&](int st) {
     if constexpr (T::kConvV) {
       constexpr int kPieces = kStage * D / 8;  // 16-byte pieces of a V stage
-      constexpr int kPpr = BLK / 8, kSh = kPpr == 2 ? 3 : 2;
       char* vl = v_lds0 + (st % kRing) * kVBytes;
-      const bool tail = kStage * (st + 1) > kv_len;
 #pragma unroll
       for (int i0 = 0; i0 < kPieces; i0 += kThreads) {
         const int i = i0 + tid;
         if (kPieces % kThreads != 0 && i >= kPieces) break;
         const u32x4 w = *reinterpret_cast<const u32x4*>(vl + i * 16);
-        u32x4 live = {~0u, ~0u, ~0u, ~0u};
-        if (tail) {
-          const int blk = i / (D * kPpr), rem = i % (D * kPpr);
-          const int d = rem / kPpr, slot = rem % kPpr;
-          const int k0 = kStage * st + blk * BLK + 8 * (slot ^ ((d >> kSh) & (kPpr - 1)));
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            live[e] = (k0 + 2 * e < kv_len ? 0xffffu : 0u) | (k0 + 2 * e + 1 < kv_len ? 0xffff0000u : 0u);
-        }
         u32x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = conv_word(w[e], live[e]);
+        for (int e = 0; e < 4; ++e) o[e] = conv_word(w[e]);
         *reinterpret_cast<u32x4*>(vl + i * 16) = o;
       }
     }
@@ -683,8 +669,12 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
   // 1 .. kVAhead-2 and K stages 2 .. kKAhead-2 issued, P(0) and S(1)
   // computed, and V stage kVAhead-1 and K stage kKAhead-1 issued once every
   // wave has read K stage 0.
-  Ids ids0 = load_ids<BLK>(bt, 0, last_blk, p.num_blocks);
-  Ids ids1 = load_ids<BLK>(bt, 1, last_blk, p.num_blocks);
+  Ids ids0 = load_ids_raw<BLK>(bt, 0, last_blk);
+  Ids ids1 = load_ids_raw<BLK>(bt, 1, last_blk);
+  Ids ids2 = load_ids_raw<BLK>(bt, 2, last_blk);
+  Ids ids3 = load_ids_raw<BLK>(bt, 3, last_blk);
+  ids0 = clamp_ids(ids0, p.num_blocks);
+  ids1 = clamp_ids(ids1, p.num_blocks);
   issue_k(0, ids0);
   issue_v(0, ids0);
   commit(0, 0);
@@ -698,11 +688,13 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
   Ids idsv = ids1;  // V stage s-1 goes with K stage s
 #pragma unroll
   for (int s2 = 2; s2 < kKAhead - 1; ++s2) {  // direct loads only (fp8: kKAhead - 1 == 2)
-    const Ids idsk = load_ids<BLK>(bt, s2, last_blk, p.num_blocks);
+    const Ids idsk = clamp_ids(s2 == 2 ? ids2 : ids3, p.num_blocks);
     if (s2 - 1 < nst) issue_v(s2 - 1, idsv);
     if (s2 < nst) issue_k(s2, idsk);
     idsv = idsk;
   }
+  const Ids ids4raw = load_ids_raw<BLK>(bt, kKAhead - 1, last_blk);
+  const Ids ids5raw = load_ids_raw<BLK>(bt, kKAhead, last_blk);
   lgkm_barrier();
   if (nsub > 0) {
     KOps k0;
@@ -719,7 +711,7 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
   // B_{-1}: K stage 0 has been read (its buffer takes K stage kKAhead-1);
   // a converted V stage 1 must have landed
   ring_barrier(kKAhead - 2 < nst);
-  Ids idsk = load_ids<BLK>(bt, kKAhead - 1, last_blk, p.num_blocks);
+  Ids idsk = clamp_ids(ids4raw, p.num_blocks);
   int pend_k = -1, pend_v = -1;  // fp8 stages waiting in registers
   if (kVAhead - 1 < nst) {
     issue_v(kVAhead - 1, idsv);
@@ -730,7 +722,7 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     pend_k = kKAhead - 1;
   }
   idsv = idsk;                                                 // V stage X+kVAhead at B_X
-  idsk = load_ids<BLK>(bt, kKAhead, last_blk, p.num_blocks);  // K stage X+kKAhead at B_X
+  idsk = clamp_ids(ids5raw, p.num_blocks);  // K stage X+kKAhead at B_X
 
   // step j (every branch is uniform over the wave): PV(j) with pcur,
   // P(j+1) = softmax(S(j+1)) into pnext, S(j+2) = QK(j+2)
@@ -825,7 +817,7 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
           asm volatile("" : "+v"(x[i]));
         }
         if (next) ko.k[c] = *reinterpret_cast<const F*>(kl_next + (kx ^ (c << 5)));
-        if (conv && c % (QS / 4) == QS / 4 - 1) cw[c / (QS / 4)] = conv_word(cw[c / (QS / 4)], ~0u);
+        if (conv && c % (QS / 4) == QS / 4 - 1) cw[c / (QS / 4)] = conv_word(cw[c / (QS / 4)]);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (conv) *reinterpret_cast<u32x4*>(cp) = cw;
@@ -894,8 +886,15 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     stage_end(X);
   }
   if constexpr (T::kConvV) {
-    // a value the conversion could not keep: redo these rows exactly
-    const int big = max(vmax.x, vmax.y) >= 0x4780;  // |v| >= 65536 as bf16, inf or NaN
+    // a V value beyond f16 range became inf in the conversion and made some
+    // accumulator non-finite (inf, or NaN where its weight was 0): redo
+    // these rows exactly
+    float fs = 0.f;
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) fs += acc[n][i];
+    const int big = !__builtin_isfinite(fs);
     if (__syncthreads_or(big)) return false;
   }
 
