@@ -34,9 +34,6 @@ Parity status of each function (how it is pinned, in tests/test_oracle_pins.py):
                                  constant V, single key), library SDPA.
 * suffix_prefill_attention .... pinned: P=0 vs library causal SDPA; prefix reuse
                                  equals full recompute (page A §03 2,000/1,900).
-* cascade_decode_attention .... pinned: equals decode_attention on aliased tables
-                                 (groups, members shorter than the prefix, empty
-                                 sequences); identical shared keys give the mean.
 """
 from __future__ import annotations
 
@@ -52,7 +49,6 @@ __all__ = [
     "gather",
     "decode_attention",
     "suffix_prefill_attention",
-    "cascade_decode_attention",
 ]
 
 
@@ -198,64 +194,6 @@ def decode_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         for h in (range(hq) if heads is None else heads):
             g = h // group
             out[s, h] = _softmax_attend(q[s, h].astype(np.float64), kc[:, g, :], vc[:, g, :], scale)
-    return out
-
-
-# --------------------------------------------------------------------------
-# Cascade decode over a shared prefix (page A §03: a common prefix is stored
-# once; page B "RadixAttention": many requests share one system prompt). The
-# shared keys are gathered once per group and every member's queries attend to
-# them; each member then attends to its own later tokens; the two partial
-# softmaxes are merged by their log-sum-exp.
-# --------------------------------------------------------------------------
-def _partial(q_row: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float):
-    """(max score, sum of exp(score - max), sum of exp(score - max) * value)
-    over the given keys; (-inf, 0, 0) for none."""
-    if keys.shape[0] == 0:
-        return -np.inf, 0.0, np.zeros(values.shape[-1])
-    s = scale * (keys @ q_row)
-    m = s.max()
-    e = np.exp(s - m)
-    return m, e.sum(), e @ values
-
-
-def cascade_decode_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
-                             block_tables: np.ndarray, context_lens: np.ndarray,
-                             group_starts: np.ndarray, shared_lens: np.ndarray, scale: float,
-                             fp8: bool = False, k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
-    """Group g = sequences group_starts[g] .. group_starts[g+1]-1 shares the
-    first shared_lens (whole blocks) tokens, read through the group's first
-    table. Member s attends to the shared keys 0 .. min(L, len_s)-1 and to its
-    own keys L .. len_s-1; out = (e^{m1-m} o1 + e^{m2-m} o2) / (e^{m1-m} l1 +
-    e^{m2-m} l2) with m = max(m1, m2). A sequence of length 0 gives zeros."""
-    num_seqs, hq, d = q.shape
-    hkv = k_cache.shape[2]
-    bsz = k_cache.shape[1]
-    group = hq // hkv
-    out = np.zeros((num_seqs, hq, d))
-    for g in range(len(group_starts) - 1):
-        first, last = int(group_starts[g]), int(group_starts[g + 1])
-        if last <= first:
-            continue
-        L = max(int(shared_lens[first]), 0)
-        L -= L % bsz
-        ks = gather(k_cache, block_tables[first], L, fp8, k_scale)
-        vs = gather(v_cache, block_tables[first], L, fp8, v_scale)
-        for s in range(first, last):
-            n = max(int(context_lens[s]), 0)
-            if n == 0:
-                continue
-            ls = min(L, n)
-            ko = gather(k_cache, block_tables[s], n, fp8, k_scale)[ls:]
-            vo = gather(v_cache, block_tables[s], n, fp8, v_scale)[ls:]
-            for h in range(hq):
-                qr = q[s, h].astype(np.float64)
-                m1, l1, o1 = _partial(qr, ks[:ls, h // group, :], vs[:ls, h // group, :], scale)
-                m2, l2, o2 = _partial(qr, ko[:, h // group, :], vo[:, h // group, :], scale)
-                m = max(m1, m2)
-                f1 = 0.0 if m1 == -np.inf else np.exp(m1 - m)
-                f2 = 0.0 if m2 == -np.inf else np.exp(m2 - m)
-                out[s, h] = (f1 * o1 + f2 * o2) / (f1 * l1 + f2 * l2)
     return out
 
 

@@ -372,7 +372,13 @@ def test_chatbot_prefill_saving_arithmetic():
     assert round(100 * (1 - with_reuse / without)) >= g["saving_percent"]
 
 
-# ---------------------------------------------------------------- cascade decode
+# ---------------------------------------------------------------- grouped (shared-prefix) batches
+# The cascade decode is checked on the GPU against decode_attention on grouped
+# batches; these pins fix what those batches must be: members of a group read
+# their shared prefix through the same physical blocks (page A §03: a common
+# prefix is stored once), and reading it through aliased blocks gives exactly
+# what private copies of those blocks give (page A §02: scattered blocks are read
+# as one logical sequence).
 def _grouped(seed, groups, dtype=torch.float32, hq=4, hkv=2, d=16, b=16):
     case = workloads.make_grouped_decode_case(seed, groups, hq, hkv, d, b, dtype)
     kc, vc = oracle.append(_np(case.k_pool), _np(case.v_pool), _np(case.k_new), _np(case.v_new),
@@ -380,30 +386,49 @@ def _grouped(seed, groups, dtype=torch.float32, hq=4, hkv=2, d=16, b=16):
     return case, kc, vc
 
 
-@pytest.mark.parametrize("groups", [
+GROUPINGS = [
     [([40, 70, 33], 32)],                          # one group, two shared blocks
     [([40, 70, 33], 32), ([5], 0), ([100, 90], 64)],
     [([20, 50], 48), ([0, 17], 16), ([16, 33], 16)],  # members shorter than / equal to the prefix, an empty one
-])
-def test_cascade_equals_decode_on_aliased_tables(groups):
-    case, kc, vc = _grouped(77, groups)
-    ref = oracle.decode_attention(_np(case.q), kc, vc, case.block_tables.numpy(), case.context_lens.numpy(),
-                                  case.scale)
-    got = oracle.cascade_decode_attention(_np(case.q), kc, vc, case.block_tables.numpy(),
-                                          case.context_lens.numpy(), case.meta["group_starts"].numpy(),
-                                          case.meta["shared_lens"].numpy(), case.scale)
-    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+]
 
 
-def test_cascade_identical_shared_keys_give_mean_of_values():
-    # every key equal (shared and own): the softmax is uniform, out = mean of V
-    case, kc, vc = _grouped(5, [([48, 64, 80], 32)])
-    kc[:] = 0.3
-    ctx = case.context_lens.numpy()
-    got = oracle.cascade_decode_attention(_np(case.q), kc, vc, case.block_tables.numpy(), ctx,
-                                          case.meta["group_starts"].numpy(), case.meta["shared_lens"].numpy(),
-                                          case.scale)
-    for s in range(case.num_seqs):
-        vals = oracle.gather(vc, case.block_tables[s].numpy(), int(ctx[s]))
-        for h in range(case.num_q_heads):
-            np.testing.assert_allclose(got[s, h], vals[:, h // 2, :].mean(axis=0), rtol=0, atol=1e-12)
+@pytest.mark.parametrize("groups", GROUPINGS)
+def test_grouped_batches_alias_their_shared_blocks(groups):
+    case, _, _ = _grouped(77, groups)
+    gs, sl, bt = case.meta["group_starts"].numpy(), case.meta["shared_lens"].numpy(), case.block_tables.numpy()
+    b = case.block_size
+    assert gs[0] == 0 and gs[-1] == case.num_seqs and (np.diff(gs) >= 0).all()
+    for g in range(len(gs) - 1):
+        members = range(gs[g], gs[g + 1])
+        assert len({int(sl[s]) for s in members}) == 1  # one shared length per group, whole blocks
+        n = int(sl[gs[g]]) // b
+        assert int(sl[gs[g]]) % b == 0
+        for s in members:
+            assert (bt[s, :n] == bt[gs[g], :n]).all()
+    # no block is shared across groups
+    for g in range(len(gs) - 1):
+        for h in range(g + 1, len(gs) - 1):
+            a = {int(x) for s in range(gs[g], gs[g + 1]) for x in bt[s, :(int(case.context_lens[s]) + b - 1) // b]}
+            c = {int(x) for s in range(gs[h], gs[h + 1]) for x in bt[s, :(int(case.context_lens[s]) + b - 1) // b]}
+            assert not a & c
+
+
+@pytest.mark.parametrize("groups", GROUPINGS)
+def test_aliased_prefix_equals_private_copies(groups):
+    case, kc, vc = _grouped(78, groups)
+    bt, ctx = case.block_tables.numpy().copy(), case.context_lens.numpy()
+    ref = oracle.decode_attention(_np(case.q), kc, vc, bt, ctx, case.scale)
+    # give every member after the first its own copy of each shared block
+    gs, sl = case.meta["group_starts"].numpy(), case.meta["shared_lens"].numpy()
+    kcs, vcs = [kc], [vc]
+    nb = kc.shape[0]
+    for g in range(len(gs) - 1):
+        n = int(sl[gs[g]]) // case.block_size
+        for s in range(gs[g] + 1, gs[g + 1]):
+            for j in range(n):
+                kcs.append(kc[bt[s, j]][None]); vcs.append(vc[bt[s, j]][None])
+                bt[s, j] = nb
+                nb += 1
+    got = oracle.decode_attention(_np(case.q), np.concatenate(kcs), np.concatenate(vcs), bt, ctx, case.scale)
+    assert np.array_equal(got, ref)
