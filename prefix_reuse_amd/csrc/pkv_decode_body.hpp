@@ -60,9 +60,11 @@ struct ChunkRegs {
   uint32_t v[NT][VW];
 };
 
+// K rows at or past the chunk's `live` tokens are not read (their scores are
+// masked): a sequence's last block is read only as far as it holds tokens.
 template <typename TC, int D, int BLK>
 __device__ __forceinline__ void load_chunk(ChunkRegs<TC, D>& r, const TC* kbase, const TC* vbase,
-                                           int blk0, int blk1, int hk, int hkv, int c16, int g) {
+                                           int blk0, int blk1, int hk, int hkv, int c16, int g, int live) {
   typedef ChunkRegs<TC, D> R;
   const int64_t tile = (int64_t)BLK * D;
 #pragma unroll
@@ -70,8 +72,13 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<TC, D>& r, const TC* kbase,
     const int tok = 8 * (c16 / 4) + 4 * a + (c16 % 4);  // chunk-relative token of this A row
     const int blk = (BLK == 32 || tok < 16) ? blk0 : blk1;
     const TC* krow = kbase + ((int64_t)blk * hkv + hk) * tile + (int64_t)(tok % BLK) * D + g * R::E;
+    if (tok < live) {
 #pragma unroll
-    for (int c = 0; c < R::KN; ++c) r.k[a][c] = load_u32x4(krow + c * 4 * R::E);
+      for (int c = 0; c < R::KN; ++c) r.k[a][c] = load_u32x4(krow + c * 4 * R::E);
+    } else {
+#pragma unroll
+      for (int c = 0; c < R::KN; ++c) r.k[a][c] = u32x4{0u, 0u, 0u, 0u};
+    }
   }
   const int tokv = 8 * g;
   const int blkv = (BLK == 32 || tokv < 16) ? blk0 : blk1;
@@ -414,7 +421,7 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int log
     if constexpr (kStep) {
       if (jn < kChunk) fetch_new_token<TQ, TC, D>(nt, p, s_cur, jn, hk, c16, g);
     }
-    load_chunk<TC, D, BLK>(r, kbase, vbase, b0, b1, hk, p.hkv, c16, g);
+    load_chunk<TC, D, BLK>(r, kbase, vbase, b0, b1, hk, p.hkv, c16, g, ctx - tb);
     if constexpr (kStep) {
       if (jn < kChunk) place_new_token<TQ, TC, D>(r, nt, p);
     }
