@@ -132,6 +132,32 @@ def test_cascade_long_shared_short_private():
     assert report("cascade long shared", got[:, heads], ref[:, heads], torch.bfloat16, TOL[torch.bfloat16]) <= 1.0
 
 
+@pytest.mark.parametrize("fill", [0x00, 0xFF, 0x7F])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_cascade_any_workspace_contents(fill, dtype):
+    """The workspace needs no initial contents: whatever bytes it holds
+    (here all-0, all-1 bits and 0x7F in every byte), the result matches the
+    oracle, on the first call and bit for bit on a second one that finds
+    the first call's partials and partition info there."""
+    groups = [(lens, (shared // 16) * 16) for lens, shared in GROUPS[0]]
+    case = workloads.make_grouped_decode_case(500, groups, 32, 8, 128, 16, dtype)
+    kc, vc = pkv.caches_from_logical(case.k_pool, case.v_pool, "cuda")
+    pkv.append(case.k_new.cuda(), case.v_new.cuda(), case.slot_mapping.cuda(), kc, vc)
+    need = pkv.cascade_workspace_bytes(case.num_seqs, 32, 8, 128)
+    ws = torch.full((need,), fill, dtype=torch.uint8, device="cuda")
+    ref = oracle_decode(case)
+    print(f"workspace fill 0x{fill:02x} {dtype}", flush=True)
+    outs = []
+    for _ in range(2):
+        out = pkv.cascade_decode_attn(case.q.cuda(), kc, vc, case.block_tables.cuda(), case.context_lens.cuda(),
+                                      case.meta["group_starts"].cuda(), case.meta["shared_lens"].cuda(), case.scale,
+                                      workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(out.clone())
+        assert report(f"cascade workspace 0x{fill:02x}", np64(out), ref, dtype, TOL[dtype]) <= 1.0
+    assert torch.equal(outs[0], outs[1])
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_cascade_random_groupings(seed):
     """Seeded random batches: 1-12 groups of 1-9 sequences, shared prefixes of
