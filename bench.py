@@ -517,7 +517,7 @@ def measured_peaks(torch, dev, stream) -> dict:
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.pkv_peak_stream_read.argtypes = [vp, i64, vp, i32, vp]
     lib.pkv_peak_tile_gather.argtypes = [vp, i64, vp, i32, vp, i32, vp]
-    lib.pkv_peak_mfma_bf16.argtypes = [i32, i32, vp, vp]
+    lib.pkv_peak_mfma_bf16.argtypes = [i32, i32, vp, vp, vp]
     for f in (lib.pkv_peak_stream_read, lib.pkv_peak_tile_gather, lib.pkv_peak_mfma_bf16):
         f.restype = ctypes.c_int
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
@@ -550,9 +550,17 @@ def measured_peaks(torch, dev, stream) -> dict:
     del buf, ids
     torch.cuda.empty_cache()
     blocks, iters = cus * 4, 4000
-    ms = best(lambda: lib.pkv_peak_mfma_bf16(blocks, iters, sink.data_ptr(), hs), reps=5)
+    clock = torch.zeros(2, dtype=torch.int64, device=dev)
+    ms = best(lambda: lib.pkv_peak_mfma_bf16(blocks, iters, sink.data_ptr(), clock.data_ptr(), hs), reps=5)
     flops = blocks * 4 * 4 * iters * 32768
     out["mfma_bf16_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+    cycles, ticks = (int(x) for x in clock.cpu().tolist())  # the last launch's first wave
+    if ticks > 0:
+        # shader clock under full matrix load, and the MFMA rate it allows
+        # (1,024 FLOP per cycle per SIMD, 4 SIMDs per CU)
+        ghz = cycles / (ticks * 10.0)
+        out["shader_clock_ghz_under_mfma"] = round(ghz, 3)
+        out["mfma_bf16_tflops_at_that_clock"] = round(cus * 4 * 1024 * ghz * 1e9 / 1e12, 1)
     out["probe"] = ("libpkv_peak.so: 4 GiB streamed once with 16-byte loads; 524,288 random 4 KiB tiles of a "
                     "2 GiB buffer, one wave per tile, 8 waves per CU; 16 waves per CU each issuing "
                     f"{4 * iters} v_mfma_f32_32x32x16_bf16 in 4 independent chains; best of several launches")

@@ -10,7 +10,10 @@
 //                        pattern of the paged decode (one (block, KV head) tile
 //                        of K or V per load group)
 //  pkv_peak_mfma_bf16    back-to-back v_mfma_f32_32x32x16_bf16 on every SIMD,
-//                        four independent accumulators per wave
+//                        four independent accumulators per wave; the first
+//                        wave also reads the shader clock counter and the
+//                        100 MHz constant counter around its loop, which
+//                        gives the shader clock under full matrix load
 //
 // Each kernel folds what it reads or computes into a value it stores only
 // under a condition the inputs never meet, so nothing is optimised away and
@@ -66,7 +69,13 @@ __global__ __launch_bounds__(64) void tile_gather_kernel(const char* __restrict_
   if (acc == 0x9e3779b9u) sink[0] = acc;
 }
 
-__global__ __launch_bounds__(kThreads) void mfma_bf16_kernel(int32_t iters, uint32_t* sink) {
+__global__ __launch_bounds__(kThreads) void mfma_bf16_kernel(int32_t iters, uint32_t* sink, uint64_t* clock) {
+  const bool stamp = clock != nullptr && blockIdx.x == 0 && threadIdx.x < 64;
+  uint64_t t0 = 0, r0 = 0;
+  if (stamp) {
+    t0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
   const uint32_t seed = threadIdx.x * 2654435761u + blockIdx.x;
   bf16x8 a, b;
 #pragma unroll
@@ -86,6 +95,14 @@ __global__ __launch_bounds__(kThreads) void mfma_bf16_kernel(int32_t iters, uint
 #pragma unroll
   for (int i = 0; i < 16; ++i) t += s[i];
   if (t == -1.0f) sink[0] = __float_as_uint(t);  // sums of non-negative products: never -1
+  if (stamp) {  // the loop's results are summed above, so the stamps follow every product
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0) {
+      clock[0] = t1 - t0;  // shader clock cycles
+      clock[1] = r1 - r0;  // ticks of the 100 MHz counter
+    }
+  }
 }
 
 }  // namespace
@@ -114,11 +131,12 @@ int pkv_peak_tile_gather(const void* buf, int64_t num_tiles, const int32_t* ids,
 }
 
 // `blocks` work-groups of 4 waves, each wave issuing 4 * iters matrix
-// products of 32x32x16 (32,768 FLOP each).
-int pkv_peak_mfma_bf16(int32_t blocks, int32_t iters, void* sink, void* stream) {
+// products of 32x32x16 (32,768 FLOP each). clock (nullable, two uint64):
+// the first wave's shader clock cycles and 100 MHz ticks over its loop.
+int pkv_peak_mfma_bf16(int32_t blocks, int32_t iters, void* sink, void* clock, void* stream) {
   if (!sink || blocks < 1 || iters < 1) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(mfma_bf16_kernel, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream, iters,
-                     static_cast<uint32_t*>(sink));
+                     static_cast<uint32_t*>(sink), static_cast<uint64_t*>(clock));
   return (int)hipGetLastError();
 }
 
