@@ -10,12 +10,13 @@
 //  * Balanced, persistent partition. Every 32-token chunk of every sequence
 //    is one unit of work; for each KV head (and group of up to 16 query heads)
 //    a fixed number of one-wave work-groups - as many as the chip holds at
-//    once - each take an equal, contiguous range of the chunks in sequence
-//    order. A wave keeps its softmax state across the chunks of a sequence and
-//    writes a result only when it leaves the sequence: the final output if it
-//    saw the whole sequence, else an unnormalised partial (O, m, l) that a
-//    small combine kernel merges in wave order. Lengths that differ by 8x
-//    therefore cost nothing in balance, and no wave idles on an empty split.
+//    once - each take a contiguous range of ceil(total / waves) of the chunks
+//    in sequence order (the last waves of a head may get fewer, or none). A
+//    wave keeps its softmax state across the chunks of a sequence and writes
+//    a result only when it leaves the sequence: the final output if it saw the
+//    whole sequence, else an unnormalised partial (O, m, l) that a small
+//    combine kernel merges in wave order. Lengths that differ by 8x therefore
+//    cost nothing in balance.
 //  * The whole GQA group (up to 16 query heads) is served from one read of K
 //    and V. Both products run on the matrix cores with operands loaded
 //    straight from global memory in 16-byte pieces, all of a chunk's loads
