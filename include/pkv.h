@@ -173,7 +173,8 @@ int pkv_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_te
  * until the process ends. The call never allocates or frees memory.
  *  - A batch whose pkv_decode_workspace_bytes(...) exceeds 32 MiB is rejected
  *    with PKV_ERR_WORKSPACE before anything is launched (at 8 KV heads,
- *    d = 128 and 256 compute units: up to ~500 sequences of 32 query heads).
+ *    d = 128 and 256 compute units: up to 1,759 sequences of 32 query heads,
+ *    752 of 64).
  *  - Every call on one GPU shares that GPU's array and nothing in it needs
  *    clearing; calls that overlap on one GPU (different streams, or different
  *    threads without ordering) race on it and give wrong results. Calls
