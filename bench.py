@@ -807,6 +807,9 @@ def main() -> int:
                        "unique_kv_bytes": ub, "logical_kv_bytes": lb},
             "cascade_us": round(c_ms * 1e3, 2), "plain_decode_us": round(p_ms * 1e3, 2),
             "plain_decode_unique_gbs": round(ub / (p_ms * 1e-3) / 1e9, 1),
+            # the K/V bytes the step attends to (shared blocks counted once per sequence), per second
+            "logical_kv_gbs": round(lb / (c_ms * 1e-3) / 1e9, 1),
+            "tokens_per_s": round(sc.num_seqs / (c_ms * 1e-3), 1),  # one decoded token per sequence
             "roofline": with_measured({"kernel": "pkv_cascade_decode_attn (shared part + decode_kernel + combine)",
                                        "bound": "hbm", "achieved": round(ub / (c_ms * 1e-3) / 1e9, 1),
                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
