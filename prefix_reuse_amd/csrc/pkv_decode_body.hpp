@@ -105,8 +105,9 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<TC, D>& r, const TC* kbase,
 // exactly as pkv_append converts them (bit copy; for fp8, e4m3fn(x / scale)).
 // fetch_new_token issues their loads before the chunk's own (both arrive in
 // one round trip), place_new_token swaps the values into the chunk registers,
-// and store_new_token writes them to the cache slot that the chunk load read,
-// so the cache ends as an append would leave it.
+// and store_new_token writes them to the cache slot that the chunk load read
+// (once the wave's range is done), so the cache ends as an append would
+// leave it.
 template <typename TQ, typename TC, int D>
 struct NewToken {
   static constexpr bool kFp8 = std::is_same<TC, uint8_t>::value;
@@ -200,7 +201,7 @@ __device__ __forceinline__ void place_new_token(ChunkRegs<TC, D>& r, NewToken<TQ
 }
 
 // Writes the placed values to the newest token's cache slot. Issued after the
-// chunk's products, when the chunk's own loads of those lines have returned.
+// wave's range (the chunk's own loads of those lines have long returned).
 template <typename TQ, typename TC, int D, int BLK>
 __device__ __forceinline__ void store_new_token(const NewToken<TQ, TC, D>& nt, const DecodeParams& p, int jn,
                                                 TC* kbase, TC* vbase, int blk0, int blk1, int hk, int c16, int g) {
@@ -406,6 +407,13 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int log
 
   start_seq();
   int seq_start = s_first_chunk;  // global index of s_cur's first chunk
+  // Decode step: the stores of the newest token's K and V wait until the
+  // wave's range is done (or until the next sequence's newest token comes).
+  // Stores count in the same vector-memory counter as loads, so a store
+  // issued mid-range would make the wait for the next chunk's loads wait for
+  // it too.
+  NewToken<TQ, TC, D> pend;
+  int pend_jn = -1, pend_b0 = 0, pend_b1 = 0;
   for (int c = c0; c < c1; ++c) {
     // ---- load the chunk ----
     const int jb = tb / BLK;
@@ -498,8 +506,15 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int log
     }
 
     if constexpr (kStep) {
-      if (jn < kChunk && hchunk == 0)
-        store_new_token<TQ, TC, D, BLK>(nt, p, jn, const_cast<TC*>(kbase), const_cast<TC*>(vbase), b0, b1, hk, c16, g);
+      if (jn < kChunk && hchunk == 0) {
+        if (pend_jn >= 0)
+          store_new_token<TQ, TC, D, BLK>(pend, p, pend_jn, const_cast<TC*>(kbase), const_cast<TC*>(vbase), pend_b0,
+                                          pend_b1, hk, c16, g);
+        pend = nt;
+        pend_jn = jn;
+        pend_b0 = b0;
+        pend_b1 = b1;
+      }
     }
 
     // ---- advance ----
@@ -517,6 +532,11 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int log
       bt = table_of(s_cur);
       start_seq();
     }
+  }
+  if constexpr (kStep) {
+    if (pend_jn >= 0)
+      store_new_token<TQ, TC, D, BLK>(pend, p, pend_jn, const_cast<TC*>(kbase), const_cast<TC*>(vbase), pend_b0,
+                                      pend_b1, hk, c16, g);
   }
 }
 
