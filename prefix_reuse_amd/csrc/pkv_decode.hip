@@ -40,15 +40,15 @@ namespace pkv {
 namespace {
 
 // kStep: the decode step's form, which also appends each sequence's newest
-// token (DecodeParams::k_new). It, and the f32 cache's form, need more
-// registers than the 168 that three waves per SIMD allow; the partition runs
-// two per SIMD anyway.
+// token (DecodeParams::k_new). The partition runs two waves per SIMD, so
+// every form may use the registers of two (several need more than the 168
+// that three would leave).
 // Work-group i is logical wave i: the hardware hands consecutive work-groups
 // to the eight XCDs in turn, so XCD k runs waves w = k (mod 8) of every KV
 // head. (Remapping so that each XCD took one KV head measured 1.1 % slower on
 // the Llama-shaped batch; outputs do not depend on the placement.)
 template <typename TQ, typename TC, int D, int BLK, bool kStep>
-__global__ __launch_bounds__(64, (kStep || std::is_same<TC, float>::value) ? 2 : 3) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64, 2) void decode_kernel(DecodeParams p) {
   decode_wave<TQ, TC, D, BLK, kStep>(p, blockIdx.x, threadIdx.x);
 }
 

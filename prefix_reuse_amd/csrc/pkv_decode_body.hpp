@@ -318,8 +318,10 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int log
   const int per_wave = (total + p.waves_per_head - 1) / p.waves_per_head;
   const int c0 = w * per_wave;
   const int c1 = min(c0 + per_wave, total);
-  // per-sequence partition info, written once for the combine kernel
-  if (logical == 0) {
+  // per-sequence partition info, written once for the combine kernel, by wave 0
+  // after its own range (its stores would otherwise hold up its first loads)
+  auto write_partition_info = [&]() {
+    if (logical != 0) return;
     int run = 0;
     for (int b = 0; b < p.num_seqs; b += 64) {
       const int s = b + lane;
@@ -332,8 +334,11 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int log
       }
       run = __shfl(incl, 63);
     }
+  };
+  if (c0 >= c1) {
+    write_partition_info();
+    return;
   }
-  if (c0 >= c1) return;
   // first sequence of the range: the one whose chunks contain c0
   int s_cur = 0, s_first_chunk = 0;
   {
@@ -381,28 +386,52 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int log
 
   // write this wave's result for s_cur: final output if it saw the whole
   // sequence, else an unnormalised partial in slot (w + s_cur)
-  auto finish_seq = [&](bool whole) {
-    float l = l_run + __shfl_xor(l_run, 16);
-    l += __shfl_xor(l, 32);
+  // A result of a sequence the range leaves before its end is kept in
+  // registers and written once the next one is complete (or the range is
+  // done): a store counts in the vector-memory counter with the loads, so one
+  // issued before the next sequence's loads would make their wait cover it.
+  f32x4 pend_acc[NT];
+  float pend_m = 0.f, pend_l = 0.f;
+  int pend_s = -1;
+  bool pend_whole = false;
+  auto write_result = [&](const f32x4* a, float m, float l, int s, bool whole) {
     if (!hvalid) return;
     const int qh = hk * p.group + hchunk * 16 + c16;
     if (whole) {
       const float inv = p.v_scale / l;
-      TQ* o = reinterpret_cast<TQ*>(p.out) + s_cur * p.o_s0 + qh * p.o_s1;
+      TQ* o = reinterpret_cast<TQ*>(p.out) + s * p.o_s0 + qh * p.o_s1;
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         typedef __attribute__((__vector_size__(4 * sizeof(TQ)))) TQ TQx4;
         TQx4 v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = from_f32<TQ>(acc[n][i] * inv);
+        for (int i = 0; i < 4; ++i) v[i] = from_f32<TQ>(a[n][i] * inv);
         *reinterpret_cast<TQx4*>(o + 16 * n + 4 * g) = v;
       }
     } else {
-      const int64_t row = (int64_t)(w + s_cur) * p.hq + qh;
+      const int64_t row = (int64_t)(w + s) * p.hq + qh;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(p.ws_o + row * D + 16 * n + 4 * g) = acc[n];
-      if (g == 0) { p.ws_ml[row * 2] = m_run; p.ws_ml[row * 2 + 1] = l; }
+      for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(p.ws_o + row * D + 16 * n + 4 * g) = a[n];
+      if (g == 0) { p.ws_ml[row * 2] = m; p.ws_ml[row * 2 + 1] = l; }
     }
+  };
+  auto finish_seq = [&](bool whole, bool last) {
+    float l = l_run + __shfl_xor(l_run, 16);
+    l += __shfl_xor(l, 32);
+    if (pend_s >= 0) {
+      write_result(pend_acc, pend_m, pend_l, pend_s, pend_whole);
+      pend_s = -1;
+    }
+    if (last) {
+      write_result(acc, m_run, l, s_cur, whole);
+      return;
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) pend_acc[n] = acc[n];
+    pend_m = m_run;
+    pend_l = l;
+    pend_s = s_cur;
+    pend_whole = whole;
   };
 
   start_seq();
@@ -521,7 +550,7 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int log
     tb += kChunk;
     if (tb >= ctx || c + 1 == c1) {
       const int nch = (ctx + kChunk - 1) / kChunk;
-      finish_seq(!p.shared_lens && seq_start >= c0 && seq_start + nch <= c1);  // cascade: always a partial
+      finish_seq(!p.shared_lens && seq_start >= c0 && seq_start + nch <= c1, c + 1 == c1);  // cascade: always a partial
       if (c + 1 == c1) break;
       seq_start += nch;
       do {  // next non-empty sequence
@@ -538,6 +567,7 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int log
       store_new_token<TQ, TC, D, BLK>(pend, p, pend_jn, const_cast<TC*>(kbase), const_cast<TC*>(vbase), pend_b0,
                                       pend_b1, hk, c16, g);
   }
+  write_partition_info();
 }
 
 }  // namespace
