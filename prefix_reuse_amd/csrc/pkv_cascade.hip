@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kThreads, 1) void cascade_kernel(PrefillParams sp, 
   }
   const int dwg = xcd_remap(wg - shared_wgs, (int)gridDim.x - shared_wgs);
   const int v = dwg * kWaves + __builtin_amdgcn_readfirstlane((int)threadIdx.x / 64);
-  if (v < dp.total_wgs) decode_wave<TQ, TC, D, BLK>(dp, v, (int)threadIdx.x % 64);
+  if (v < dp.total_wgs) decode_wave<TQ, TC, D, BLK, false, true>(dp, v, (int)threadIdx.x % 64);
 }
 
 template <typename TQ, typename TC, int D, int BLK>

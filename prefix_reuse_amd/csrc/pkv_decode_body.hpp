@@ -290,7 +290,11 @@ __device__ __forceinline__ int wave_scan(int x, int lane) {
 
 // One wave of the decode: logical wave index `logical` of the partition, on
 // lane `lane` (0..63) of a wave that runs nothing else.
-template <typename TQ, typename TC, int D, int BLK, bool kStep = false>
+// kIdsAhead: each chunk's block ids are fetched while the chunk before it in
+// the same sequence loads. Measured on the Llama-shaped batch, this makes the
+// step form 1.3 us faster and the cascade's decode waves ~2 us faster, but the
+// plain decode 2.7 us slower, so the plain decode keeps fetching them in turn.
+template <typename TQ, typename TC, int D, int BLK, bool kStep = false, bool kIdsAhead = false>
 __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int logical, const int lane) {
   typedef typename QFrag<TQ, TC, D>::T QT;
   typedef ChunkRegs<TC, D> R;
@@ -443,12 +447,21 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int log
   // it too.
   NewToken<TQ, TC, D> pend;
   int pend_jn = -1, pend_b0 = 0, pend_b1 = 0;
+  int nb0 = 0, nb1 = 0;   // block ids of the next chunk, fetched during this one
+  bool have_next = false;  // (when it lies in the same sequence)
   for (int c = c0; c < c1; ++c) {
     // ---- load the chunk ----
     const int jb = tb / BLK;
-    int b0 = bt[jb], b1 = b0;
-    if constexpr (BLK == 16) {
-      if ((jb + 1) * BLK < ctx) b1 = bt[jb + 1];  // only entries that hold live tokens
+    int b0, b1;
+    if (kIdsAhead && have_next) {
+      b0 = nb0;
+      b1 = nb1;
+    } else {
+      b0 = bt[jb];
+      b1 = b0;
+      if constexpr (BLK == 16) {
+        if ((jb + 1) * BLK < ctx) b1 = bt[jb + 1];  // only entries that hold live tokens
+      }
     }
     b0 = min(max(b0, 0), p.num_blocks - 1);
     b1 = min(max(b1, 0), p.num_blocks - 1);
@@ -459,6 +472,17 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int log
       if (jn < kChunk) fetch_new_token<TQ, TC, D>(nt, p, s_cur, jn, hk, c16, g);
     }
     load_chunk<TC, D, BLK>(r, kbase, vbase, b0, b1, hk, p.hkv, c16, g, ctx - tb);
+    // the next chunk's block ids, if it is in this sequence: fetched now, so
+    // that its loads need not wait for them
+    have_next = kIdsAhead && tb + kChunk < ctx && c + 1 < c1;
+    if (have_next) {
+      const int jn2 = (tb + kChunk) / BLK;
+      nb0 = bt[jn2];
+      nb1 = nb0;
+      if constexpr (BLK == 16) {
+        if ((jn2 + 1) * BLK < ctx) nb1 = bt[jn2 + 1];
+      }
+    }
     if constexpr (kStep) {
       if (jn < kChunk) place_new_token<TQ, TC, D>(r, nt, p);
     }
