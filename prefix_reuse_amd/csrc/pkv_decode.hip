@@ -49,7 +49,7 @@ namespace {
 // the Llama-shaped batch; outputs do not depend on the placement.)
 template <typename TQ, typename TC, int D, int BLK, bool kStep>
 __global__ __launch_bounds__(64, 2) void decode_kernel(DecodeParams p) {
-  decode_wave<TQ, TC, D, BLK, kStep, kStep>(p, blockIdx.x, threadIdx.x);
+  decode_wave<TQ, TC, D, BLK, kStep, kStep, true>(p, blockIdx.x, threadIdx.x);
 }
 
 // Merge the partials of the sequences that several waves shared, in wave

@@ -294,7 +294,13 @@ __device__ __forceinline__ int wave_scan(int x, int lane) {
 // the same sequence loads. Measured on the Llama-shaped batch, this makes the
 // step form 1.3 us faster and the cascade's decode waves ~2 us faster, but the
 // plain decode 2.7 us slower, so the plain decode keeps fetching them in turn.
-template <typename TQ, typename TC, int D, int BLK, bool kStep = false, bool kIdsAhead = false>
+// kSeqLanes: lane i keeps what the range walk needs of sequence i < 64 (its own
+// tokens, shared prefix, chunks and their running sum) from the first pass, so
+// that finding the first sequence and moving to the next read no memory. It
+// makes the decode and step forms ~0.6 us faster and the cascade ~0.4 us slower
+// (its kernel is already short of registers), so the cascade goes without.
+template <typename TQ, typename TC, int D, int BLK, bool kStep = false, bool kIdsAhead = false,
+          bool kSeqLanes = false>
 __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int logical, const int lane) {
   typedef typename QFrag<TQ, TC, D>::T QT;
   typedef ChunkRegs<TC, D> R;
@@ -311,12 +317,32 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int log
   const int nh = min(16, p.group - hchunk * 16);
 
   // ---- partition: total chunks, this wave's range, its first sequence ----
-  int total = 0;
+  int total = 0, own64 = 0, sh64 = 0, ch64 = 0, incl64 = 0;
   for (int b = 0; b < p.num_seqs; b += 64) {
     const int s = b + lane;
-    int ch = s < p.num_seqs ? (own_of<BLK>(p, s, cap) + kChunk - 1) / kChunk : 0;
-    total += __shfl(wave_scan(ch, lane), 63);
+    int own = 0, sh = 0;
+    if (s < p.num_seqs) {
+      const int cx = ctx_of(p, s, cap);
+      sh = shared_of<BLK>(p, s, cx);
+      own = cx - sh;
+    }
+    const int ch = (own + kChunk - 1) / kChunk;
+    const int incl = wave_scan(ch, lane);
+    if (kSeqLanes && b == 0) {
+      own64 = own;
+      sh64 = sh;
+      ch64 = ch;
+      incl64 = incl;
+    }
+    total += __shfl(incl, 63);
   }
+  // own and shared-prefix tokens of sequence s, from the lanes when kept there
+  auto own_at = [&](int s) {
+    return kSeqLanes && s < 64 ? __builtin_amdgcn_readlane(own64, s) : own_of<BLK>(p, s, cap);
+  };
+  auto shared_at = [&](int s) {
+    return kSeqLanes && s < 64 ? __builtin_amdgcn_readlane(sh64, s) : shared_of<BLK>(p, s, ctx_of(p, s, cap));
+  };
   total = __builtin_amdgcn_readfirstlane(total);
   if (total == 0) return;
   const int per_wave = (total + p.waves_per_head - 1) / p.waves_per_head;
@@ -345,7 +371,12 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int log
   }
   // first sequence of the range: the one whose chunks contain c0
   int s_cur = 0, s_first_chunk = 0;
-  {
+  if (kSeqLanes && p.num_seqs <= 64) {
+    // c0 < total, so some lane's running sum passes c0
+    const int l0 = __builtin_ctzll(__ballot(lane < p.num_seqs && incl64 > c0));
+    s_cur = l0;
+    s_first_chunk = __shfl(incl64 - ch64, l0);
+  } else {
     int run = 0;
     for (int b = 0; b < p.num_seqs; b += 64) {
       const int s = b + lane;
@@ -373,10 +404,8 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int log
   f32x4 acc[NT];
   float m_run, l_run;
   // ctx counts this kernel's tokens of s_cur; bt starts at the first of them
-  auto table_of = [&](int s) {
-    return p.block_tables + (int64_t)s * p.bt_s0 + shared_of<BLK>(p, s, ctx_of(p, s, cap)) / BLK;
-  };
-  int ctx = own_of<BLK>(p, s_cur, cap);
+  auto table_of = [&](int s) { return p.block_tables + (int64_t)s * p.bt_s0 + shared_at(s) / BLK; };
+  int ctx = own_at(s_cur);
   int tb = (c0 - s_first_chunk) * kChunk;
   const int32_t* bt = table_of(s_cur);
 
@@ -579,7 +608,7 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, const int log
       seq_start += nch;
       do {  // next non-empty sequence
         ++s_cur;
-        ctx = own_of<BLK>(p, s_cur, cap);
+        ctx = own_at(s_cur);
       } while (ctx == 0);
       tb = 0;
       bt = table_of(s_cur);
