@@ -105,3 +105,17 @@ def test_step_random_batches(seed):
     kc0, vc0 = pkv.caches_from_logical(case.k_pool, case.v_pool, "cuda")
     a, s = two_ways(case, kc0, vc0, case.q.cuda(), case.k_new.cuda(), case.v_new.cuda())
     assert_same(a, s)
+
+
+@pytest.mark.parametrize("nseq", [64, 65, 130])
+def test_step_batches_around_one_wave_of_sequences(nseq):
+    """The step form over batches on both sides of 64 sequences (the first 64
+    sequences' lengths are kept in lanes, the rest read from memory): bit for
+    bit against append + decode, caches included."""
+    rng = np.random.default_rng(970 + nseq)
+    lens = [int(x) for x in rng.integers(0, 400, nseq)]
+    lens[int(rng.integers(nseq))] = 0
+    case = workloads.make_decode_case(970 + nseq, lens, 32, 8, 128, 16, torch.bfloat16)
+    kc0, vc0 = pkv.caches_from_logical(case.k_pool, case.v_pool, "cuda")
+    a, s = two_ways(case, kc0, vc0, case.q.cuda(), case.k_new.cuda(), case.v_new.cuda())
+    assert_same(a, s)

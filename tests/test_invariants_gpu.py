@@ -102,3 +102,28 @@ def test_poisoned_slots_never_reach_outputs():
     pcase = workloads.make_prefill_case(906, [3, 0, 40], [5, 9, 1], 32, 8, 128, 16, torch.bfloat16,
                                         extra_free_blocks=4)
     assert torch.isfinite(gpu_prefill(pcase).out.float()).all()
+
+
+@pytest.mark.parametrize("nseq", [63, 64, 65, 130])
+@pytest.mark.parametrize("waves", [0, 7, 150])
+def test_decode_batches_around_one_wave_of_sequences(nseq, waves, monkeypatch):
+    """The decode's waves find their sequences through per-lane copies of the
+    first 64 sequences' lengths and through memory for the rest: batches of 63
+    to 130 ragged sequences (empty ones included), under several wave counts
+    (0: the default), against the oracle; and the default partition's result
+    within a few fp32 ulps of the one-wave-per-head walk."""
+    rng = np.random.default_rng(960 + nseq)
+    lens = [int(x) for x in rng.integers(0, 300, nseq)]
+    for s in rng.choice(nseq, 4, replace=False):
+        lens[int(s)] = 0
+    case = workloads.make_decode_case(960 + nseq, lens, 32, 8, 128, 16, torch.float16)
+    if waves:
+        monkeypatch.setenv("PKV_DECODE_WAVES", str(waves))
+    got = np64(gpu_decode(case).out)
+    monkeypatch.setenv("PKV_DECODE_WAVES", "8")
+    walk = np64(gpu_decode(case).out)
+    monkeypatch.delenv("PKV_DECODE_WAVES")
+    assert report(f"{nseq} seqs, waves {waves or 'default'}", got, oracle_decode(case), torch.float16,
+                  TOL[torch.float16]) <= 1.0
+    assert report(f"{nseq} seqs, waves {waves or 'default'} vs one wave per head", got, walk, torch.float16,
+                  1e-3) <= 1.0
