@@ -17,6 +17,10 @@ constexpr int kRowsWg = kRowsWave * kWaves;
 constexpr int kStage = 64;     // keys per LDS stage = two 32-key sub-tiles
 constexpr int kRing = 4;       // LDS buffers per operand (stage s lives in buffer s % kRing)
 constexpr float kLazy = 8.0f;  // log2 headroom before the running max moves
+// bf16 cache, fast pass: the full steps take no row maximum. A row's max moves
+// only once one of its P values passes kPCap, seen as a lane's 16 P values
+// summing past 16 kPCap (each P then stays far inside f16 range).
+constexpr float kPCap = 64.0f;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(4))) const int32_t sconst_i32;  // read with scalar loads
@@ -773,33 +777,43 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
       u32x4 cw = {};
       if (conv) cw = *reinterpret_cast<const u32x4*>(cp);
       constexpr int kE = 16 / (2 * NT);  // elements handled per value product
+      // kConvV: no row maximum here; the exponentials below use the running
+      // max as it stands and P(j+1) is checked after them (below). A score
+      // that outgrew the max by more than 2^128 makes P infinite; the
+      // accumulators then end non-finite and the exact pass redoes the rows.
+      constexpr bool kNoMax = T::kConvV;
       float mx = sc[0];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           acc[n] = mfma32x32x16(vo.v[u][n], pcur.hi[u], acc[n]);
-          const int i0 = (u * NT + n) * kE;
+          if constexpr (!kNoMax) {
+            const int i0 = (u * NT + n) * kE;
 #pragma unroll
-          for (int e = 0; e < kE; ++e) mx = fmaxf(mx, sc[i0 + e]);
-          asm volatile("" : "+v"(mx));
+            for (int e = 0; e < kE; ++e) mx = fmaxf(mx, sc[i0 + e]);
+            asm volatile("" : "+v"(mx));
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
       if (next) load_v(bv, t + 1, vo);
       __builtin_amdgcn_sched_barrier(0);
-      {  // the other 16 keys of this row sit in lane l ^ 32
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c2;  // c2 > 0: max commutes
-      }
-      const bool grow = mx > m_run + kLazy;
-      const bool rescale = __any(grow);
+      bool rescale = false;
       float alpha = 1.f;
-      if (rescale) {
-        const float m_new = grow ? mx : m_run;
-        alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 for rows that keep their max
-        m_run = m_new;
-        l_run *= alpha;
+      if constexpr (!kNoMax) {
+        {  // the other 16 keys of this row sit in lane l ^ 32
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c2;  // c2 > 0: max commutes
+        }
+        const bool grow = mx > m_run + kLazy;
+        rescale = __any(grow);
+        if (rescale) {
+          const float m_new = grow ? mx : m_run;
+          alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 for rows that keep their max
+          m_run = m_new;
+          l_run *= alpha;
+        }
       }
       // score products, each followed by 16/QS exponentials of P(j+1) and,
       // with `next`, the read of the K operand it has just consumed
@@ -821,16 +835,51 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
         __builtin_amdgcn_sched_barrier(0);
       }
       if (conv) *reinterpret_cast<u32x4*>(cp) = cw;
-      // row sum and packing of P(j+1)
-      float part[8];
+      if constexpr (kNoMax) {
+        // row sum of P(j+1); when a lane's sum passes 16 kPCap, the rows whose
+        // largest P passed kPCap move their max so that it becomes 1, and P,
+        // l and (at the end of the step) the accumulators are scaled to match
+        auto psum = [&]() {
+          float part[8];
 #pragma unroll
-      for (int pr = 0; pr < 8; ++pr) {  // elements 2pr, 2pr+1
-        const int h = pr / 4, e = 2 * (pr % 4);
-        pnext.hi[h][e] = (VOp)x[2 * pr];
-        pnext.hi[h][e + 1] = (VOp)x[2 * pr + 1];
-        part[pr] = x[2 * pr] + x[2 * pr + 1];
+          for (int pr = 0; pr < 8; ++pr) part[pr] = x[2 * pr] + x[2 * pr + 1];
+          return ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+        };
+        float lsum = psum();
+        rescale = __any(!(lsum <= 16.f * kPCap));
+        if (rescale) {
+          float px = x[0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) px = fmaxf(px, x[i]);
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(px), __float_as_uint(px), false, false);
+          px = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+          const float m_new = px > kPCap ? m_run + __builtin_amdgcn_logf(px) : m_run;  // log2
+          alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 for rows that keep their max
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] *= alpha;
+          lsum = psum();
+        }
+        l_run += lsum;
+#pragma unroll
+        for (int pr = 0; pr < 8; ++pr) {  // packing of P(j+1): elements 2pr, 2pr+1
+          const int h = pr / 4, e = 2 * (pr % 4);
+          pnext.hi[h][e] = (VOp)x[2 * pr];
+          pnext.hi[h][e + 1] = (VOp)x[2 * pr + 1];
+        }
+      } else {
+        // row sum and packing of P(j+1)
+        float part[8];
+#pragma unroll
+        for (int pr = 0; pr < 8; ++pr) {  // elements 2pr, 2pr+1
+          const int h = pr / 4, e = 2 * (pr % 4);
+          pnext.hi[h][e] = (VOp)x[2 * pr];
+          pnext.hi[h][e + 1] = (VOp)x[2 * pr + 1];
+          part[pr] = x[2 * pr] + x[2 * pr + 1];
+        }
+        l_run += ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
       }
-      l_run += ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
       sc = s2;
       if (rescale) {
 #pragma unroll

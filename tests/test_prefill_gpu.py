@@ -134,3 +134,33 @@ def test_prefill_bf16_large_values(big):
     assert np.isfinite(np64(run.out)).all()
     scale = max(1.0, abs(big))
     assert report(f"big {big}", np64(run.out), ref, torch.bfloat16, TOL[torch.bfloat16] * scale) <= 1.0
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("shape", ["gradual", "jump"])
+def test_prefill_scores_that_grow_along_the_keys(dtype, shape):
+    """Softmax maxima that keep moving while the stage loop runs. "gradual":
+    every cached key row is scaled by 1 + 3t/P, so a row's largest score grows
+    by ~10 (base 2) along the prefix and the running max has to move inside
+    the loop's full steps. "jump": one late cached key of request 0 is 40 x the
+    query of suffix row 0 (head 0), a score hundreds of units (base 2) above
+    every earlier one, far past what a running max can absorb in fp32 without
+    moving. Both against the oracle."""
+    case = workloads.make_prefill_case(610, [1500, 700], [64, 40], 8, 2, 128, 16, dtype)
+    b = case.block_size
+    k = case.k_pool.float()
+    if shape == "gradual":
+        for r, plen in enumerate(case.prefix_lens.tolist()):
+            for t in range(plen):
+                blk = int(case.block_tables[r, t // b])
+                k[blk, t % b] *= 1.0 + 3.0 * t / plen
+    else:
+        t = 1400
+        blk = int(case.block_tables[0, t // b])
+        k[blk, t % b, 0] = 40.0 * case.q_suffix[0, 0].float()
+    case.k_pool = k.to(dtype)
+    print(f"prefill {dtype} keys {shape}", flush=True)
+    run = gpu_prefill(case)
+    ref = oracle_prefill(case)
+    assert np.isfinite(np64(run.out)).all()
+    assert report(f"keys {shape} {dtype}", np64(run.out), ref, dtype, TOL[dtype]) <= 1.0
