@@ -164,3 +164,24 @@ def test_prefill_scores_that_grow_along_the_keys(dtype, shape):
     ref = oracle_prefill(case)
     assert np.isfinite(np64(run.out)).all()
     assert report(f"keys {shape} {dtype}", np64(run.out), ref, dtype, TOL[dtype]) <= 1.0
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_prefill_heavy_tailed_key_scales(seed):
+    """Every cached and new key row scaled by exp(N(0, 1.5)): row maxima jump up
+    and down along the keys, so the bf16 fast pass's full steps move the
+    running max (and rescale P) many times. Against the oracle."""
+    rng = np.random.default_rng(620 + seed)
+    case = workloads.make_prefill_case(620 + seed, [900, 1300, 260], [70, 33, 128], 16, 4, 128, 16, torch.bfloat16)
+    k = case.k_pool.float()
+    live = ~torch.isnan(k[:, :, 0, 0])
+    f = torch.from_numpy(np.exp(rng.normal(0.0, 1.5, size=tuple(live.shape)))).float()
+    k = torch.where(live[:, :, None, None], k * f[:, :, None, None], k)
+    case.k_pool = k.to(torch.bfloat16)
+    fn = torch.from_numpy(np.exp(rng.normal(0.0, 1.5, size=(case.k_new.shape[0],)))).float()
+    case.k_new = (case.k_new.float() * fn[:, None, None]).to(torch.bfloat16)
+    print(f"prefill heavy-tailed key scales, seed {seed}", flush=True)
+    run = gpu_prefill(case)
+    ref = oracle_prefill(case)
+    assert np.isfinite(np64(run.out)).all()
+    assert report(f"heavy-tailed keys {seed}", np64(run.out), ref, torch.bfloat16, TOL[torch.bfloat16]) <= 1.0
