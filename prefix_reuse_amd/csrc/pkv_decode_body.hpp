@@ -293,7 +293,7 @@ __device__ __forceinline__ int wave_scan(int x, int lane) {
 // kIdsAhead: each chunk's block ids are fetched while the chunk before it in
 // the same sequence loads. Measured on the Llama-shaped batch, this makes the
 // step form 1.3 us faster and the cascade's decode waves ~2 us faster, but the
-// plain decode 2.7 us slower, so the plain decode keeps fetching them in turn.
+// plain decode 2.1-2.7 us slower, so the plain decode keeps fetching them in turn.
 // kSeqLanes: lane i keeps what the range walk needs of sequence i < 64 (its own
 // tokens, shared prefix, chunks and their running sum) from the first pass, so
 // that finding the first sequence and moving to the next read no memory. It

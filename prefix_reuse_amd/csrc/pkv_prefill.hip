@@ -30,14 +30,17 @@
 //    its operands from LDS first, computes a softmax while they arrive, then
 //    issues its 24 (16) products back to back.
 //  * Precision of P in the PV product: with f16 operands P is rounded to f16
-//    (11 bits, P is in [0, 2^8] thanks to the lazy rescale below). With bf16
+//    (11 bits; P stays in [0, 2^10] thanks to the lazy rescale below). With bf16
 //    operands P would carry only 8 bits - too few for 2e-3 on short contexts -
 //    so P goes in as bf16(P) + bf16(P - bf16(P)): two products on the matrix
 //    cores. fp8 V is converted exactly to f16 while staging.
 //  * Online softmax in base 2 with the scale folded into one FMA per score and
 //    the raw v_exp_f32 (results below 2^-126 flush to 0); the running max moves
 //    only when a row's max grows by more than 2^8 (lazy rescale), so the
-//    output accumulators are rarely rescaled. The causal mask is applied only
+//    output accumulators are rarely rescaled. The bf16 cache's fast pass takes
+//    no row max in its full steps at all: it checks P's row sums after the
+//    exponentials and moves a row's max only once one of its P values passes
+//    2^6 (an infinite P sends the work-group to the exact pass). The causal mask is applied only
 //    on key tiles that reach past the wave's first token.
 #include "pkv_prefill_body.hpp"
 
