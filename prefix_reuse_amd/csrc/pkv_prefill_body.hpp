@@ -837,8 +837,14 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
       if (conv) *reinterpret_cast<u32x4*>(cp) = cw;
       if constexpr (kNoMax) {
         // row sum of P(j+1); when a lane's sum passes 16 kPCap, the rows whose
-        // largest P passed kPCap move their max so that it becomes 1, and P,
-        // l and (at the end of the step) the accumulators are scaled to match
+        // largest P passed kPCap move their max by that P's binary exponent,
+        // so that P, l and (at the end of the step) the accumulators scale by
+        // an exact power of two, whatever the size of the jump (the kernel
+        // keeps fp32 denormals, so 2^-128 is exact; a factor computed with
+        // v_exp_f32 would flush to 0 below 2^-126 and take the row's new
+        // largest P with it). An infinite P (a jump past 2^128) is left as it
+        // is: the accumulators then end non-finite and the exact pass redoes
+        // the work-group.
         auto psum = [&]() {
           float part[8];
 #pragma unroll
@@ -853,9 +859,10 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
           for (int i = 1; i < 16; ++i) px = fmaxf(px, x[i]);
           const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(px), __float_as_uint(px), false, false);
           px = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-          const float m_new = px > kPCap ? m_run + __builtin_amdgcn_logf(px) : m_run;  // log2
-          alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 for rows that keep their max
-          m_run = m_new;
+          // px = f 2^e with f in [0.5, 1); e = 0 for rows that keep their max
+          const int e = px > kPCap && px <= 3.4028235e38f ? __builtin_amdgcn_frexp_expf(px) : 0;
+          m_run += (float)e;
+          alpha = __builtin_ldexpf(1.f, -e);  // 2^-e, exact (a denormal past 2^-126)
           l_run *= alpha;
 #pragma unroll
           for (int i = 0; i < 16; ++i) x[i] *= alpha;

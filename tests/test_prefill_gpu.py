@@ -1,4 +1,6 @@
 """Suffix-prefill parity: the HIP path against the oracle."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -185,3 +187,28 @@ def test_prefill_heavy_tailed_key_scales(seed):
     ref = oracle_prefill(case)
     assert np.isfinite(np64(run.out)).all()
     assert report(f"heavy-tailed keys {seed}", np64(run.out), ref, torch.bfloat16, TOL[torch.bfloat16]) <= 1.0
+
+
+@pytest.mark.parametrize("jump", [100.0, 118.0, 124.0, 126.0, 126.5, 127.0, 127.5, 128.0, 131.0])
+def test_prefill_score_jump_near_float_range(jump):
+    """One late cached key of request 0 set to a multiple of the query of suffix
+    row 0 (head 0), so that its score (base 2, scale included) is `jump` units
+    above zero: P computed against the running max is finite but up to 2^128,
+    and moving the max must not lose it (a factor of 2^-jump computed as exp2
+    flushes to 0 below 2^-126). Against the oracle, bf16 and f16."""
+    for dtype in (torch.bfloat16, torch.float16):
+        case = workloads.make_prefill_case(611, [1500, 300], [40, 20], 8, 2, 128, 16, dtype)
+        b = case.block_size
+        q0 = case.q_suffix[0, 0].float()
+        c = case.scale * math.log2(math.e)
+        alpha = jump / (float((q0 * q0).sum()) * c)
+        k = case.k_pool.float()
+        t = 1400
+        blk = int(case.block_tables[0, t // b])
+        k[blk, t % b, 0] = alpha * q0
+        case.k_pool = k.to(dtype)
+        print(f"prefill {dtype} score jump {jump}", flush=True)
+        run = gpu_prefill(case)
+        ref = oracle_prefill(case)
+        assert np.isfinite(np64(run.out)).all()
+        assert report(f"jump {jump} {dtype}", np64(run.out), ref, dtype, TOL[dtype]) <= 1.0
