@@ -9,7 +9,7 @@ import torch
 import oracle
 import prefix_reuse_amd as pkv
 import workloads
-from _helpers import (TOL, fp8_inputs_from_pools, gpu_decode, gpu_fp8_decode, np64, oracle_decode,
+from _helpers import (TOL, bits, fp8_inputs_from_pools, gpu_decode, gpu_fp8_decode, np64, oracle_decode,
                       oracle_fp8_caches, report)
 
 pytestmark = pytest.mark.gpu
@@ -67,6 +67,51 @@ def test_decode_zero_length_rows_are_zero():
     assert np.array_equal(out[1], np.zeros_like(out[1]))
     ref = oracle_decode(case)
     assert report("zero-len", out, ref, torch.bfloat16, TOL[torch.bfloat16]) <= 1.0
+
+
+@pytest.mark.parametrize("fill", [0x00, 0xFF, 0x7F, None])
+def test_decode_any_workspace_contents(fill):
+    """The workspace (partials of the sequences that several waves share, and
+    the partition info the merge reads) needs no initial contents. Whatever
+    bytes it holds (all-0, all-1 bits, 0x7F in every byte, seeded random
+    bytes), three decode calls in a row, a smaller batch on the same
+    workspace between the first two, and a decode step after them match the
+    oracle, and the repeated calls agree bit for bit."""
+    dtype = torch.float16
+    lens = [3000, 1, 0, 2500, 700, 4100, 33]
+    case = workloads.make_decode_case(79, lens, 32, 8, 128, 16, dtype)
+    small = workloads.make_decode_case(80, [900, 0, 40], 32, 8, 128, 16, dtype)
+    need = max(pkv.decode_workspace_bytes(c.num_seqs, 32, 8, 128, c.block_tables.shape[1], 16) for c in (case, small))
+    if fill is None:
+        ws = torch.from_numpy(np.random.default_rng(81).integers(0, 256, need, dtype=np.uint8)).cuda()
+    else:
+        ws = torch.full((need,), fill, dtype=torch.uint8, device="cuda")
+    print(f"workspace fill {fill}", flush=True)
+
+    def on_gpu(c):
+        kc, vc = pkv.caches_from_logical(c.k_pool, c.v_pool, "cuda")
+        pkv.append(c.k_new.cuda(), c.v_new.cuda(), c.slot_mapping.cuda(), kc, vc)
+        return c.q.cuda(), kc, vc, c.block_tables.cuda(), c.context_lens.cuda()
+
+    q, kc, vc, bt, cl = on_gpu(case)
+    sq, skc, svc, sbt, scl = on_gpu(small)
+    ref, ref_small = oracle_decode(case), oracle_decode(small)
+    outs = []
+    for i in range(3):
+        out = pkv.decode_attn(q, kc, vc, bt, cl, case.scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert report(f"workspace {fill} call {i}", np64(out), ref, dtype, TOL[dtype]) <= 1.0
+        outs.append(out.clone())
+        if i == 0:
+            out_small = pkv.decode_attn(sq, skc, svc, sbt, scl, small.scale, workspace=ws)
+            torch.cuda.synchronize()
+            assert report(f"workspace {fill} small batch", np64(out_small), ref_small, dtype, TOL[dtype]) <= 1.0
+    for o in outs[1:]:
+        assert np.array_equal(bits(o), bits(outs[0]))
+    kc2, vc2 = pkv.caches_from_logical(case.k_pool, case.v_pool, "cuda")
+    out_s = pkv.decode_step_attn(q, case.k_new.cuda(), case.v_new.cuda(), kc2, vc2, bt, cl, case.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out_s), bits(outs[0]))
 
 
 def test_decode_strided_q_and_out():
