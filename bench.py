@@ -1,27 +1,33 @@
 #!/usr/bin/env python3
 """Benchmark of the paged-KV attention hot path on one MI355X.
 
-One step = one serving step of the decode workload: append the newest token's
-K and V for every sequence (pkv_append), then paged decode attention over the
-whole cache (pkv_decode_attn). Workload: batch 64, 32 query / 8 KV heads,
-head dim 128, fp16 KV, 16-token blocks, context lengths uniform in
-[512, 4096], physical blocks shuffled (Llama-3-8B-shaped single layer).
+One step = one serving step of the decode workload in one call
+(pkv_decode_step_attn): the newest token's K and V of every sequence go into
+the cache and each query attends to the whole cache, as pkv_append followed
+by pkv_decode_attn would do. Workload: batch 64, 32 query / 8 KV heads, head
+dim 128, fp16 KV, 16-token blocks, context lengths uniform in [512, 4096],
+physical blocks shuffled (Llama-3-8B-shaped single layer).
 
 Printed as one JSON line:
   value      decode KV-read GB/s = K+V bytes the step must read / step time
-  roofline   the decode kernel's own duration (HIP events on its stream)
+  roofline   the decode call's own duration (HIP events on its stream)
              against the HBM peak; traffic from rocprofv3 counters when they
              match the current kernel sources (else null)
   suffix_prefill  the same for the suffix-prefill workload (16 requests x
-             1,900 cached + 100 new tokens, bf16): TFLOP/s against bf16 MFMA peak
+             1,900 cached + 100 new tokens, bf16): TFLOP/s against bf16 MFMA
+             peak, timed cold (inputs evicted) and warm
+  suffix_prefill_fp8_kv  the same workload over an fp8 e4m3fn cache
+  shared_prefix_decode  256 sequences on one 1,000-token shared prefix
+             (cascade decode), GB/s of unique KV bytes against the HBM peak
   long_context_fp8  8 sequences x 100,000 tokens x 32 layers with an fp8
              e4m3fn cache: append + decode for every layer per step, GB/s of
              KV read, and one layer's decode call against the HBM peak
   cpu_baseline    the CPU oracle timed on this host's cores (one core, and N worker
              processes) on the decode, suffix-prefill and long-context workloads
   measured_peaks  ceilings this GPU reaches with probe kernels (stream read, 4 KiB
-             tile gather, bf16 MFMA loop); each roofline also gives its fraction of
-             the measured ceiling
+             tile gather, bf16 MFMA loop, and the shader clock under that loop);
+             each roofline also gives its fraction of the measured ceiling
+  clocks_rocm_smi  rocm-smi's clock readout, sampled while the decode step runs
 
 Inputs are synthetic (seeded N(0,1)), resident in HBM before timing starts.
 """
@@ -31,6 +37,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 from pathlib import Path
@@ -72,6 +79,35 @@ def warm_clocks(torch, fn, seconds=0.5):
         for _ in range(10):
             fn()
         torch.cuda.synchronize()
+
+
+def smi_clocks(torch, fn, limit_s=20.0):
+    """Clocks as rocm-smi reports them (`--showclocks --json`), sampled in a
+    child process while fn runs back to back; None if the tool is missing or
+    prints no JSON."""
+    try:
+        proc = subprocess.Popen(["rocm-smi", "--showclocks", "--json"], stdout=subprocess.PIPE,
+                                stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+    t0 = time.perf_counter()
+    while proc.poll() is None and time.perf_counter() - t0 < limit_s:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+    try:
+        text, _ = proc.communicate(timeout=max(1.0, limit_s - (time.perf_counter() - t0)))
+    except subprocess.TimeoutExpired:
+        proc.kill()
+        proc.communicate()
+        return None
+    i = text.find("{")
+    if proc.returncode != 0 or i < 0:
+        return None
+    try:
+        return json.loads(text[i:])
+    except ValueError:
+        return None
 
 
 def time_launches(torch, stream, fn, n) -> float:
@@ -664,6 +700,7 @@ def main() -> int:
     kv_bytes = case.kv_read_bytes()
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
 
+    clocks = smi_clocks(torch, step)
     # the same step as two calls (pkv_append, then pkv_decode_attn)
     two_ms = time_launches(torch, stream, step_two_calls, args.steps)
     # the decode call alone (its two kernels), back to back on its stream
@@ -698,6 +735,9 @@ def main() -> int:
         "step_as_two_calls_us": round(two_ms * 1e3, 2),
         "roofline": roofline,
         "measured_peaks": peaks or None,
+        "clocks_rocm_smi": None if clocks is None else {
+            "sampled": "rocm-smi --showclocks --json, run while the decode step ran back to back",
+            "reading": clocks},
     }
 
     # ---------------- suffix prefill: append suffix + prefill ----------------
