@@ -96,6 +96,29 @@ def test_config4_suffix_prefill_sampled_rows():
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("dtype,block", [(torch.bfloat16, 16), (torch.float16, 32)])
+def test_prefill_long_prefix_sampled_rows(dtype, block):
+    """Prefixes of 30,000 and 12,345 cached tokens (each work-group runs
+    hundreds of stages through its LDS ring), checked on sampled rows. q is
+    scaled by 4 and every V row carries a per-(KV head, dim) mean in
+    [0.5, 2] with a random sign, so that |out| is of order 1 over these long
+    contexts and an all-zero or garbage output fails the gate."""
+    case = workloads.make_prefill_case(640 + block, [30000, 12345], [64, 37], 32, 8, 128, block, dtype)
+    g = torch.Generator().manual_seed(641)
+    mean = (torch.rand(8, 128, generator=g) * 1.5 + 0.5) * (torch.randint(0, 2, (8, 128), generator=g) * 2 - 1)
+    case.v_pool = (case.v_pool.float() + mean).to(dtype)  # unused slots stay NaN
+    case.v_new = (case.v_new.float() + mean).to(dtype)
+    case.q_suffix = (case.q_suffix.float() * 4).to(dtype)
+    print(f"{dtype} B={block}", flush=True)
+    out = np64(gpu_prefill(case).out)
+    assert np.isfinite(out).all()
+    rows = sorted({0, 1, 62, 63, 64, 65, 99, 100} | set(np.random.default_rng(642).choice(101, 6, replace=False).tolist()))
+    ref = oracle_prefill(case, rows=rows)
+    assert np.abs(ref[rows]).max() > 0.5
+    assert report(f"long prefix {dtype} B={block}", out[rows], ref[rows], dtype, TOL[dtype]) <= 1.0
+
+
+@pytest.mark.slow
 def test_config4_reuse_equals_full_recompute_on_gpu():
     """The 2,000-token request with 1,900 cached gives the same 100 rows as
     prefilling all 2,000 (prefix reuse does not change the output)."""
