@@ -119,6 +119,38 @@ def test_prefill_long_prefix_sampled_rows(dtype, block):
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("q_dtype", [torch.bfloat16, torch.float16])
+def test_prefill_fp8_long_prefix_sampled_rows(q_dtype):
+    """The long-prefix case over an fp8 cache (prefix and suffix rows
+    quantized by append, per-tensor scales): 24,000 and 9,000 cached tokens,
+    q scaled by 4, V with a per-(KV head, dim) mean, sampled rows against
+    the oracle over the same codes."""
+    case = workloads.make_prefill_case(650, [24000, 9000], [48, 29], 32, 8, 128, 32, torch.float32)
+    g = torch.Generator().manual_seed(651)
+    mean = (torch.rand(8, 128, generator=g) * 1.5 + 0.5) * (torch.randint(0, 2, (8, 128), generator=g) * 2 - 1)
+    case.v_pool = case.v_pool + mean  # unused slots stay NaN
+    case.v_new = case.v_new + mean
+    case.q_suffix = case.q_suffix * 4
+    inp = fp8_inputs_from_pools(case, q_dtype)
+    kc, vc = nan_fp8_caches(case)
+    pkv.append(inp.rows_k.cuda(), inp.rows_v.cuda(), inp.slots.cuda(), kc, vc, inp.k_scale, inp.v_scale)
+    q = case.q_suffix.to(q_dtype)
+    print(f"fp8, q {q_dtype}", flush=True)
+    out = np64(pkv.suffix_prefill_attn(q.cuda(), kc, vc, case.block_tables.cuda(), case.prefix_lens.cuda(),
+                                       case.suffix_lens.cuda(), case.scale, k_scale=inp.k_scale,
+                                       v_scale=inp.v_scale))
+    torch.cuda.synchronize()
+    assert np.isfinite(out).all()
+    rows = sorted({0, 1, 46, 47, 48, 49, 75, 76} | set(np.random.default_rng(652).choice(77, 6, replace=False).tolist()))
+    ek, ev = oracle_fp8_caches(case, inp)
+    ref = oracle.suffix_prefill_attention(np64(q), ek, ev, case.block_tables.numpy(), case.prefix_lens.numpy(),
+                                          case.suffix_lens.numpy(), case.scale, fp8=True, k_scale=inp.k_scale,
+                                          v_scale=inp.v_scale, rows=rows)
+    assert np.abs(ref[rows]).max() > 0.5
+    assert report(f"fp8 long prefix q {q_dtype}", out[rows], ref[rows], q_dtype, TOL["fp8"]) <= 1.0
+
+
+@pytest.mark.slow
 def test_config4_reuse_equals_full_recompute_on_gpu():
     """The 2,000-token request with 1,900 cached gives the same 100 rows as
     prefilling all 2,000 (prefix reuse does not change the output)."""
