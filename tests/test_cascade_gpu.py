@@ -132,6 +132,35 @@ def test_cascade_long_shared_short_private():
     assert report("cascade long shared", got[:, heads], ref[:, heads], torch.bfloat16, TOL[torch.bfloat16]) <= 1.0
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("dtype,b", [(torch.bfloat16, 32), (torch.float16, 16)])
+def test_cascade_long_shared_prefix_order_one_outputs(dtype, b):
+    """Two groups on shared prefixes of 20,000 and 6,000 tokens (the shared
+    part runs hundreds of stages), 24 and 9 sequences with 1-300 tokens of
+    their own. q is scaled by 4 and every V row carries a per-(KV head, dim)
+    mean in [0.5, 2] with a random sign, so that |out| is of order 1 and an
+    all-zero output fails; every sequence is checked on 4 of the 32 heads."""
+    rng = np.random.default_rng(670)
+    groups = [([20000 + int(x) for x in rng.integers(1, 301, 24)], 20000),
+              ([6000 + int(x) for x in rng.integers(1, 301, 9)], 6000)]
+    case = workloads.make_grouped_decode_case(670 + b, groups, 32, 8, 128, b, dtype)
+    g = torch.Generator().manual_seed(671)
+    mean = (torch.rand(8, 128, generator=g) * 1.5 + 0.5) * (torch.randint(0, 2, (8, 128), generator=g) * 2 - 1)
+    case.v_pool = (case.v_pool.float() + mean).to(dtype)  # unused slots stay NaN
+    case.v_new = (case.v_new.float() + mean).to(dtype)
+    case.q = (case.q.float() * 4).to(dtype)
+    print(f"{dtype} B={b}", flush=True)
+    got = np64(run_cascade(case))
+    assert np.isfinite(got).all()
+    heads = [0, 13, 22, 31]
+    ek, ev = oracle.append(np64(case.k_pool), np64(case.v_pool), np64(case.k_new), np64(case.v_new),
+                           case.slot_mapping.numpy())
+    ref = oracle.decode_attention(np64(case.q), ek, ev, case.block_tables.numpy(), case.context_lens.numpy(),
+                                  case.scale, heads=heads)
+    assert np.abs(ref[:, heads]).max() > 0.5
+    assert report(f"cascade long shared {dtype}", got[:, heads], ref[:, heads], dtype, TOL[dtype]) <= 1.0
+
+
 @pytest.mark.parametrize("fill", [0x00, 0xFF, 0x7F])
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 def test_cascade_any_workspace_contents(fill, dtype):
