@@ -13,6 +13,7 @@ Printed as one JSON line:
   roofline   the decode call's own duration (HIP events on its stream)
              against the HBM peak; traffic from rocprofv3 counters when they
              match the current kernel sources (else null)
+  step_roofline  the same for the step's one call (the value's own kernels)
   suffix_prefill  the same for the suffix-prefill workload (16 requests x
              1,900 cached + 100 new tokens, bf16): TFLOP/s against bf16 MFMA
              peak, timed cold (inputs evicted) and warm
@@ -621,7 +622,7 @@ def main() -> int:
     ap.add_argument("--no-long-context", action="store_true")
     ap.add_argument("--no-shared-prefix", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-ceiling probes")
-    ap.add_argument("--only", choices=["decode", "prefill", "prefill_fp8", "long", "shared"], default=None,
+    ap.add_argument("--only", choices=["decode", "step", "prefill", "prefill_fp8", "long", "shared"], default=None,
                     help="run only this kernel's launches (for profiler runs)")
     ap.add_argument("--ingest-profile", nargs=5, metavar=("NAME", "TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "KERNEL_REGEX"),
                     help="summarise rocprofv3 csv output into profiles/ (no GPU needed)")
@@ -650,9 +651,10 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     if args.only is not None:
-        setup = {"decode": decode_setup, "prefill": prefill_setup, "prefill_fp8": prefill_fp8_setup,
-                 "long": long_context_setup, "shared": shared_prefix_setup}[args.only]
-        call = {"decode": run_decode_call, "prefill": run_prefill_call, "prefill_fp8": run_prefill_fp8_call,
+        setup = {"decode": decode_setup, "step": decode_setup, "prefill": prefill_setup,
+                 "prefill_fp8": prefill_fp8_setup, "long": long_context_setup, "shared": shared_prefix_setup}[args.only]
+        call = {"decode": run_decode_call, "step": run_decode_step, "prefill": run_prefill_call,
+                "prefill_fp8": run_prefill_fp8_call,
                 "long": lambda pkv, t: run_long_context_decode(pkv, t, t["layers"][0]),
                 "shared": run_cascade_call}[args.only]
         t = setup(torch, pkv, workloads, dev) if args.only != "long" else setup(torch, pkv, workloads, dev, 1)
@@ -707,6 +709,7 @@ def main() -> int:
     dec_ms = time_launches(torch, stream, lambda: run_decode_call(pkv, t), args.steps)
     dec_gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
     traffic = load_traffic("decode_llama3_8b_b64_fp16", KERNEL_SOURCES)
+    step_traffic = load_traffic("decode_step_llama3_8b_b64_fp16", KERNEL_SOURCES)
     roofline = {
         "kernel": "pkv_decode_attn (decode_kernel + decode_combine_kernel)",
         "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -734,6 +737,12 @@ def main() -> int:
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "step_as_two_calls_us": round(two_ms * 1e3, 2),
         "roofline": roofline,
+        "step_roofline": with_measured({
+            "kernel": "pkv_decode_step_attn (decode_kernel in its step form + decode_combine_kernel)",
+            "bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(value / HBM_PEAK_GBS, 4),
+            "traffic": None if step_traffic is None else step_traffic["bytes_per_launch"],
+            "avg_launch_us": round(ms_per_step * 1e3, 2), "algorithmic_bytes_per_launch": kv_bytes}, hbm_meas),
         "measured_peaks": peaks or None,
         "clocks_rocm_smi": None if clocks is None else {
             "sampled": "rocm-smi --showclocks --json, run while the decode step ran back to back",
