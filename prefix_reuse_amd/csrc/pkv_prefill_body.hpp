@@ -400,24 +400,29 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
   const int tok = rvalid ? row / p.group : 0;
   const int qh = hk * p.group + (rvalid ? row % p.group : 0);
   const TQ* qrow = reinterpret_cast<const TQ*>(p.q) + (int64_t)(row_base + tok) * p.q_s0 + (int64_t)qh * p.q_s1;
-  F qf[QS];
-#pragma unroll
-  for (int c = 0; c < QS; ++c) {
-    F v = {};
-    if (rvalid) v = load_frag8(qrow + 16 * c + 8 * h0);
-    qf[c] = v;
-  }
   // the kernel's score scale c2 is positive: a negative softmax scale is
   // applied by negating q (exact), a zero one by zeroing it (every score 0)
-  if (p.q_mode != 0) {
-    const uint32_t keep = p.q_mode == 1 ? ~0u : 0u;
-#pragma unroll
-    for (int c = 0; c < QS; ++c) {
-      u32x4 w = __builtin_bit_cast(u32x4, qf[c]);
+  auto qfrag = [&](int c) -> F {
+    F v = {};
+    if (rvalid) v = load_frag8(qrow + 16 * c + 8 * h0);
+    if (p.q_mode != 0) {
+      const uint32_t keep = p.q_mode == 1 ? ~0u : 0u;
+      u32x4 w = __builtin_bit_cast(u32x4, v);
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = (w[e] & keep) ^ (keep & 0x80008000u);
-      qf[c] = __builtin_bit_cast(F, w);
+      v = __builtin_bit_cast(F, w);
     }
+    return v;
+  };
+  // The fragments stay in registers, except in the exact pass of a bf16
+  // cache, which reads them again for each score product (and, in its steps,
+  // reads the K operands only after the value products): that pass runs only
+  // for a work-group that met a V value beyond f16 range, and with these
+  // registers freed both passes fit in one kernel with no scratch.
+  F qf[QS];
+  if constexpr (!T::kSplitP) {
+#pragma unroll
+    for (int c = 0; c < QS; ++c) qf[c] = qfrag(c);
   }
   const int lim = casc ? ctx_row - 1 : P + tok;  // last key position this row may see
   const float c2 = p.qk_scale_log2;
@@ -521,7 +526,10 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
   auto qk = [&](const KOps& ko) -> f32x16 {  // S^T[key][row], unscaled
     f32x16 sc = {};
 #pragma unroll
-    for (int c = 0; c < QS; ++c) sc = mfma32x32x16(ko.k[c], qf[c], sc);
+    for (int c = 0; c < QS; ++c) {
+      if constexpr (!T::kSplitP) sc = mfma32x32x16(ko.k[c], qf[c], sc);
+      else sc = mfma32x32x16(ko.k[c], qfrag(c), sc);
+    }
     return sc;
   };
   auto pv = [&](const VOps& vo, const PFrag<FV>& pf) {  // O^T += V^T P^T
@@ -735,7 +743,9 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     VOps vo;
     KOps ko;
     if (do_pv) load_v(bv, t, vo);
-    if (do_qk) load_k(bk, t, ko);
+    if constexpr (!T::kSplitP) {
+      if (do_qk) load_k(bk, t, ko);
+    }
     float alpha = 1.f;
     bool rescale = false;
     if (do_sm) rescale = softmax(sc, 32 * (j + 1), 32 * (j + 2) > full_keys_w, pnext, alpha);
@@ -746,6 +756,9 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     if (rescale) {
 #pragma unroll
       for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+    }
+    if constexpr (T::kSplitP) {  // the exact pass: V operands dead before the K ones are read
+      if (do_qk) load_k(bk, t, ko);
     }
     if (do_qk) sc = qk(ko);
   };
