@@ -127,3 +127,29 @@ def test_decode_batches_around_one_wave_of_sequences(nseq, waves, monkeypatch):
                   TOL[torch.float16]) <= 1.0
     assert report(f"{nseq} seqs, waves {waves or 'default'} vs one wave per head", got, walk, torch.float16,
                   1e-3) <= 1.0
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("dtype,b", [(torch.float16, 16), (torch.bfloat16, 32)])
+def test_decode_four_thousand_short_sequences(dtype, b):
+    """4,096 sequences of 0-64 tokens (one in eight empty): the partition's
+    first pass runs 64 batches of sequences, most waves find their first
+    sequence in memory rather than in the lanes, and the merge runs 16,384
+    work-groups. Decode against the oracle on every sequence and head; the
+    step form bit for bit against append + decode, caches included."""
+    rng = np.random.default_rng(970 + b)
+    lens = [int(x) for x in rng.integers(1, 65, 4096)]
+    for s in rng.choice(4096, 512, replace=False):
+        lens[int(s)] = 0
+    case = workloads.make_decode_case(970 + b, lens, 32, 8, 128, b, dtype)
+    print(f"{dtype} B={b}", flush=True)
+    run = gpu_decode(case)
+    out = np64(run.out)
+    assert np.array_equal(out[np.array(lens) == 0], np.zeros_like(out[np.array(lens) == 0]))
+    assert report(f"4096 seqs {dtype}", out, oracle_decode(case), dtype, TOL[dtype]) <= 1.0
+    kc, vc = pkv.caches_from_logical(case.k_pool, case.v_pool, "cuda")
+    step = pkv.decode_step_attn(case.q.cuda(), case.k_new.cuda(), case.v_new.cuda(), kc, vc,
+                                case.block_tables.cuda(), case.context_lens.cuda(), case.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(step), bits(run.out))
+    assert np.array_equal(bits(kc), bits(run.k_cache)) and np.array_equal(bits(vc), bits(run.v_cache))
