@@ -18,6 +18,8 @@ Printed as one JSON line:
              1,900 cached + 100 new tokens, bf16): TFLOP/s against bf16 MFMA
              peak, timed cold (inputs evicted) and warm
   suffix_prefill_fp8_kv  the same workload over an fp8 e4m3fn cache
+  suffix_prefill_next_turn  one conversation's next turn (1 request, 8,000
+             cached + 100 new tokens), the key-split call against the plain one
   shared_prefix_decode  256 sequences on one 1,000-token shared prefix
              (cascade decode), GB/s of unique KV bytes against the HBM peak
   long_context_fp8  8 sequences x 100,000 tokens x 32 layers with an fp8
@@ -154,6 +156,34 @@ def prefill_setup(torch, pkv, workloads, dev):
     pkv.append(t["k_new"], t["v_new"], t["slots"], kc, vc)
     torch.cuda.synchronize()
     return t
+
+
+def next_turn_setup(torch, pkv, workloads, dev):
+    """One conversation's next turn (one request, 8,000 cached + 100 new
+    tokens), with the key-split call's workspace."""
+    case = workloads.next_turn_suffix_prefill()
+    kc, vc = pkv.caches_from_logical(case.k_pool, case.v_pool, dev)
+    t = {"case": case, "kc": kc, "vc": vc, "q": case.q_suffix.to(dev), "bt": case.block_tables.to(dev),
+         "pl": case.prefix_lens.to(dev), "sl": case.suffix_lens.to(dev)}
+    t["out"] = torch.empty_like(t["q"])
+    pkv.append(case.k_new.to(dev), case.v_new.to(dev), case.slot_mapping.to(dev), kc, vc)
+    need = pkv.suffix_prefill_workspace_bytes(case.q_suffix.shape[0], 1, case.num_q_heads, case.num_kv_heads,
+                                              case.head_dim, case.block_tables.shape[1], case.block_size)
+    t["ws"] = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    t["ws_bytes"] = need
+    torch.cuda.synchronize()
+    return t
+
+
+def run_next_turn_split(pkv, t):
+    c = t["case"]
+    pkv.suffix_prefill_attn_split(t["q"], t["kc"], t["vc"], t["bt"], t["pl"], t["sl"], c.scale, out=t["out"],
+                                  workspace=t["ws"])
+
+
+def run_next_turn_plain(pkv, t):
+    c = t["case"]
+    pkv.suffix_prefill_attn(t["q"], t["kc"], t["vc"], t["bt"], t["pl"], t["sl"], c.scale, out=t["out"])
 
 
 def prefill_fp8_setup(torch, pkv, workloads, dev):
@@ -622,7 +652,8 @@ def main() -> int:
     ap.add_argument("--no-long-context", action="store_true")
     ap.add_argument("--no-shared-prefix", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-ceiling probes")
-    ap.add_argument("--only", choices=["decode", "step", "prefill", "prefill_fp8", "long", "shared"], default=None,
+    ap.add_argument("--only", choices=["decode", "step", "prefill", "prefill_fp8", "turn", "long", "shared"],
+                    default=None,
                     help="run only this kernel's launches (for profiler runs)")
     ap.add_argument("--ingest-profile", nargs=5, metavar=("NAME", "TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "KERNEL_REGEX"),
                     help="summarise rocprofv3 csv output into profiles/ (no GPU needed)")
@@ -652,9 +683,10 @@ def main() -> int:
 
     if args.only is not None:
         setup = {"decode": decode_setup, "step": decode_setup, "prefill": prefill_setup,
-                 "prefill_fp8": prefill_fp8_setup, "long": long_context_setup, "shared": shared_prefix_setup}[args.only]
+                 "prefill_fp8": prefill_fp8_setup, "turn": next_turn_setup, "long": long_context_setup,
+                 "shared": shared_prefix_setup}[args.only]
         call = {"decode": run_decode_call, "step": run_decode_step, "prefill": run_prefill_call,
-                "prefill_fp8": run_prefill_fp8_call,
+                "prefill_fp8": run_prefill_fp8_call, "turn": run_next_turn_split,
                 "long": lambda pkv, t: run_long_context_decode(pkv, t, t["layers"][0]),
                 "shared": run_cascade_call}[args.only]
         t = setup(torch, pkv, workloads, dev) if args.only != "long" else setup(torch, pkv, workloads, dev, 1)
@@ -831,6 +863,35 @@ def main() -> int:
             "timing": "back to back",
         }
         del p8
+        torch.cuda.empty_cache()
+
+        # one conversation's next turn: the key-split call against the plain one
+        nt = next_turn_setup(torch, pkv, workloads, dev)
+        nflops = nt["case"].flops()
+        for _ in range(args.warmup):
+            run_next_turn_split(pkv, nt)
+            run_next_turn_plain(pkv, nt)
+        warm_clocks(torch, lambda: run_next_turn_split(pkv, nt))
+        ns_ms = time_launches(torch, stream, lambda: run_next_turn_split(pkv, nt), args.steps)
+        np_ms = time_launches(torch, stream, lambda: run_next_turn_plain(pkv, nt), args.steps)
+        ns_tflops = nflops / (ns_ms * 1e-3) / 1e12
+        ntraffic = load_traffic("prefill_next_turn_1x8000p100_bf16", KERNEL_SOURCES)
+        result["suffix_prefill_next_turn"] = {
+            "metric": "suffix-prefill TFLOP/s, one conversation's next turn", "value": round(ns_tflops, 2),
+            "unit": "TFLOP/s",
+            "config": {"workload": "1 request x (8,000 cached + 100 new tokens), 32/8 heads, d=128, bf16, B=16 "
+                                   "(pkv_suffix_prefill_attn_split)", "flop_per_launch": nflops,
+                       "workspace_bytes": nt["ws_bytes"]},
+            "split_us": round(ns_ms * 1e3, 2), "plain_us": round(np_ms * 1e3, 2),
+            "plain_tflops": round(nflops / (np_ms * 1e-3) / 1e12, 2),
+            "roofline": with_measured({"kernel": "prefill_split_kernel + prefill_merge_kernel", "bound": "mfma",
+                                       "achieved": round(ns_tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                                       "unit": "TFLOP/s", "frac": round(ns_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                                       "traffic": None if ntraffic is None else ntraffic["bytes_per_launch"],
+                                       "avg_launch_us": round(ns_ms * 1e3, 2)}, mfma_meas),
+            "timing": "back to back",
+        }
+        del nt
         torch.cuda.empty_cache()
 
     # ---------------- shared-prefix decode: cascade vs plain ----------------

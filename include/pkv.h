@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 5
+#define PKV_ABI_VERSION 6
 
 typedef enum {
   PKV_F32 = 0,
@@ -240,6 +240,47 @@ int pkv_suffix_prefill_attn(const pkv_tensor* q_suffix, const pkv_tensor* k_cach
                             const pkv_tensor* prefix_lens, const pkv_tensor* suffix_lens,
                             float scale, float k_scale, float v_scale, const pkv_tensor* out,
                             void* stream);
+
+/*
+ * pkv_suffix_prefill_workspace_bytes — bytes of device workspace that
+ * pkv_suffix_prefill_attn_split needs on the CURRENT device for a batch of
+ * total_suffix_tokens rows from num_requests requests: 0 when the batch
+ * needs no split, else parts * total_suffix_tokens * H_q * (head_dim + 2)
+ * floats. parts (per row tile, 2..17) comes from the shapes alone: a batch
+ * whose row tiles, ceil(total * G / 256) per KV head, give every compute unit
+ * at least half a work-group takes no split; otherwise each tile gets enough
+ * parts to fill the compute units, with prefix chunks of at least 256 keys at
+ * the table's capacity. The environment variable PKV_PREFILL_SPLITS (1..17)
+ * sets the count for both calls. num_requests does not change the size.
+ * Returns 0 on invalid sizes as well.
+ */
+size_t pkv_suffix_prefill_workspace_bytes(int64_t total_suffix_tokens, int64_t num_requests,
+                                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                          int64_t max_blocks_per_seq, int32_t block_size);
+
+/*
+ * pkv_suffix_prefill_attn_split — pkv_suffix_prefill_attn for batches with
+ * few suffix rows and long prefixes: one conversation's next turn ([C] §5,
+ * third limit: each turn of a multi-turn conversation carries every earlier
+ * turn, whose K, V are cached; [A] §03: only the new suffix is computed),
+ * which a plain launch spreads over only H_kv work-groups per 256 rows. The keys of each row tile are split:
+ * parts 0 .. parts-2 take chunks of the prefix's whole 64-key stages (every
+ * suffix row sees them all), the last part the remaining prefix keys and the
+ * suffix (causally); each part writes an unnormalised partial (O, m, l) and a
+ * second launch merges them by log-sum-exp. Same arguments, contract and
+ * result as pkv_suffix_prefill_attn (the sums run in another order, so the
+ * bits may differ within rounding), plus:
+ *  workspace     at least pkv_suffix_prefill_workspace_bytes(...) bytes
+ *                (max_blocks_per_seq = block_tables.shape[1]), 16-byte
+ *                aligned, no initial contents needed; may be NULL when that
+ *                size is 0, and the call is then pkv_suffix_prefill_attn.
+ *                Calls sharing one workspace must be ordered on one stream.
+ */
+int pkv_suffix_prefill_attn_split(const pkv_tensor* q_suffix, const pkv_tensor* k_cache,
+                                  const pkv_tensor* v_cache, const pkv_tensor* block_tables,
+                                  const pkv_tensor* prefix_lens, const pkv_tensor* suffix_lens,
+                                  float scale, float k_scale, float v_scale, void* workspace,
+                                  size_t workspace_bytes, const pkv_tensor* out, void* stream);
 
 /*
  * pkv_cascade_workspace_bytes — bytes of device workspace pkv_cascade_decode_attn

@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "LIB_PATH", "lib", "PkvError",
     "append", "decode_attn", "decode_attn_noalloc", "decode_step_attn", "suffix_prefill_attn",
-    "decode_workspace_bytes",
+    "suffix_prefill_attn_split", "suffix_prefill_workspace_bytes", "decode_workspace_bytes",
     "cascade_decode_attn", "cascade_workspace_bytes",
     "empty_caches", "caches_from_logical", "k_logical", "v_logical", "abi_version",
 ]
@@ -77,6 +77,12 @@ def _load() -> ctypes.CDLL:
     L.pkv_suffix_prefill_attn.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_float,
                                           ctypes.c_float, P, ctypes.c_void_p]
     L.pkv_suffix_prefill_attn.restype = ctypes.c_int
+    L.pkv_suffix_prefill_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                     ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]
+    L.pkv_suffix_prefill_workspace_bytes.restype = ctypes.c_size_t
+    L.pkv_suffix_prefill_attn_split.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                                ctypes.c_void_p, ctypes.c_size_t, P, ctypes.c_void_p]
+    L.pkv_suffix_prefill_attn_split.restype = ctypes.c_int
     L.pkv_cascade_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     L.pkv_cascade_workspace_bytes.restype = ctypes.c_size_t
     L.pkv_cascade_decode_attn.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float,
@@ -252,6 +258,38 @@ def suffix_prefill_attn(q_suffix: torch.Tensor, k_cache: torch.Tensor, v_cache: 
                                      float(scale), float(k_scale), float(v_scale), _ref(do),
                                      _stream(q_suffix.device))
     _check("pkv_suffix_prefill_attn", rc)
+    return out
+
+
+def suffix_prefill_workspace_bytes(total_suffix_tokens: int, num_requests: int, num_q_heads: int,
+                                   num_kv_heads: int, head_dim: int, max_blocks_per_seq: int,
+                                   block_size: int) -> int:
+    """Workspace bytes pkv_suffix_prefill_attn_split needs (0: the batch takes no split)."""
+    return lib.pkv_suffix_prefill_workspace_bytes(total_suffix_tokens, num_requests, num_q_heads, num_kv_heads,
+                                                  head_dim, max_blocks_per_seq, block_size)
+
+
+def suffix_prefill_attn_split(q_suffix: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              block_tables: torch.Tensor, prefix_lens: torch.Tensor,
+                              suffix_lens: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
+                              k_scale: float = 1.0, v_scale: float = 1.0,
+                              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """suffix_prefill_attn with the keys of each row tile split over several
+    work-groups when the batch has too few rows to fill the GPU."""
+    if out is None:
+        out = torch.empty_like(q_suffix)
+    need = suffix_prefill_workspace_bytes(q_suffix.shape[0], prefix_lens.shape[0], q_suffix.shape[1],
+                                          k_cache.shape[1], q_suffix.shape[2], block_tables.shape[1],
+                                          k_cache.shape[2])
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_suffix.device)  # no initial contents needed
+    ws_ptr, ws_bytes = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) if need else (None, 0)
+    dq, dkc, dvc, dbt, dp, dsl, do = map(_desc, (q_suffix, k_cache, v_cache, block_tables,
+                                                  prefix_lens, suffix_lens, out))
+    rc = lib.pkv_suffix_prefill_attn_split(_ref(dq), _ref(dkc), _ref(dvc), _ref(dbt), _ref(dp), _ref(dsl),
+                                           float(scale), float(k_scale), float(v_scale), ws_ptr, ws_bytes,
+                                           _ref(do), _stream(q_suffix.device))
+    _check("pkv_suffix_prefill_attn_split", rc)
     return out
 
 

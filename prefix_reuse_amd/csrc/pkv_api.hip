@@ -195,6 +195,35 @@ size_t decode_ws_bytes(int64_t num_seqs, int32_t hq, int32_t hkv, int32_t d, pkv
   return slots * hq * (size_t)(d + 2) * sizeof(float) + (size_t)num_seqs * 2 * sizeof(int32_t);
 }
 
+// Key-split suffix prefill: parts per row tile (1: no split), from what the
+// host knows. A batch whose row tiles already give every CU half a
+// work-group stays whole; otherwise each tile gets enough parts to fill the
+// CUs (at most 17: 16 chunks of the prefix and the rest), with prefix chunks
+// of at least 256 keys at the table's capacity. PKV_PREFILL_SPLITS (1..17)
+// forces the count.
+int prefill_parts(int64_t total, int32_t hq, int32_t hkv, int64_t max_blocks, int32_t block) {
+  if (const char* env = getenv("PKV_PREFILL_SPLITS")) {
+    const long forced = atol(env);
+    if (forced >= 1 && forced <= 17) return (int)forced;
+  }
+  const int64_t W = pkv::kPrefillRowsPerWg;
+  const int64_t tiles = (total * (hq / hkv) + W - 1) / W;  // row tiles of the fullest packing
+  const int64_t wgs = tiles * hkv;
+  const int64_t cus = device_cus();
+  if (wgs == 0 || 2 * wgs > cus) return 1;
+  int64_t parts = cus / wgs;
+  parts = parts < 17 ? parts : 17;
+  const int64_t by_keys = max_blocks * block / 256 + 1;
+  parts = parts < by_keys ? parts : by_keys;
+  return (int)(parts > 1 ? parts : 1);
+}
+
+// the partials of a key-split prefill: O [parts, total, H_q, d] and (m, l)
+// [parts, total, H_q, 2] floats
+size_t prefill_ws_bytes(int parts, int64_t total, int32_t hq, int32_t d) {
+  return parts > 1 ? (size_t)parts * total * hq * (size_t)(d + 2) * sizeof(float) : 0;
+}
+
 // cascade: how many work-groups share one row tile of the shared part (each
 // takes one chunk of the shared keys). The shared part runs beside the
 // private-token decode in one launch, so it needs only to finish before the
@@ -517,30 +546,13 @@ int decode_call(const pkv_tensor* q, const pkv_tensor* k_new, const pkv_tensor* 
 }
 }  // namespace pkv
 
-extern "C" {
-
-int pkv_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_tensor* v_cache,
-                    const pkv_tensor* block_tables, const pkv_tensor* context_lens, float scale,
-                    float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
-                    const pkv_tensor* out, void* stream) {
-  return pkv::decode_call(q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
-                          v_scale, workspace, workspace_bytes, nullptr, out, stream);
-}
-
-int pkv_decode_step_attn(const pkv_tensor* q, const pkv_tensor* k_new, const pkv_tensor* v_new,
-                         const pkv_tensor* k_cache, const pkv_tensor* v_cache, const pkv_tensor* block_tables,
-                         const pkv_tensor* context_lens, float scale, float k_scale, float v_scale, void* workspace,
-                         size_t workspace_bytes, const pkv_tensor* out, void* stream) {
-  if (!k_new) return fail(PKV_ERR_NULL, "k_new: descriptor is NULL");
-  if (!v_new) return fail(PKV_ERR_NULL, "v_new: descriptor is NULL");
-  return pkv::decode_call(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
-                          workspace, workspace_bytes, nullptr, out, stream);
-}
-
-int pkv_suffix_prefill_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_tensor* v_cache,
-                            const pkv_tensor* block_tables, const pkv_tensor* prefix_lens,
-                            const pkv_tensor* suffix_lens, float scale, float k_scale, float v_scale,
-                            const pkv_tensor* out, void* stream) {
+namespace {
+// pkv_suffix_prefill_attn, and with `split` pkv_suffix_prefill_attn_split
+// (which falls back to the plain launch when the shape calls for no split).
+int prefill_call(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_tensor* v_cache,
+                 const pkv_tensor* block_tables, const pkv_tensor* prefix_lens, const pkv_tensor* suffix_lens,
+                 float scale, float k_scale, float v_scale, void* workspace, size_t workspace_bytes, bool split,
+                 const pkv_tensor* out, void* stream) {
   int rc;
   CacheGeom cg;
   if ((rc = check_caches(k_cache, v_cache, &cg))) return rc;
@@ -589,9 +601,74 @@ int pkv_suffix_prefill_attn(const pkv_tensor* q, const pkv_tensor* k_cache, cons
   p.tiles_per_head = (int32_t)tiles;
   fold_scale(qk, &p.qk_scale_log2, &p.q_mode);
   p.v_scale = fp8 ? v_scale : 1.0f;
+  const int parts = split ? prefill_parts(total, (int32_t)hq, cg.hkv, p.max_blocks, cg.block) : 1;
+  if (parts > 1) {
+    const size_t need = prefill_ws_bytes(parts, total, (int32_t)hq, cg.dim);
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(PKV_ERR_WORKSPACE, "suffix prefill workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    if (!aligned16(workspace)) return fail(PKV_ERR_LAYOUT, "workspace must be 16-byte aligned");
+    if (tiles * parts * cg.hkv > INT32_MAX || total * ((hq + 7) / 8) > INT32_MAX)
+      return fail(PKV_ERR_SHAPE, "problem too large for one launch");
+    p.key_splits = parts;
+    p.tiles_per_head = (int32_t)(tiles * parts);
+    p.ws_o = reinterpret_cast<float*>(workspace);
+    p.ws_ml = p.ws_o + (size_t)parts * total * hq * cg.dim;
+    hipError_t e = pkv::launch_prefill_split(p, to_dt(q->dtype), to_dt(cg.dtype), cg.dim, cg.block,
+                                             (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
   hipError_t e = pkv::launch_prefill(p, to_dt(q->dtype), to_dt(cg.dtype), cg.dim, cg.block, (hipStream_t)stream);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_decode_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_tensor* v_cache,
+                    const pkv_tensor* block_tables, const pkv_tensor* context_lens, float scale,
+                    float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                    const pkv_tensor* out, void* stream) {
+  return pkv::decode_call(q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
+                          v_scale, workspace, workspace_bytes, nullptr, out, stream);
+}
+
+int pkv_decode_step_attn(const pkv_tensor* q, const pkv_tensor* k_new, const pkv_tensor* v_new,
+                         const pkv_tensor* k_cache, const pkv_tensor* v_cache, const pkv_tensor* block_tables,
+                         const pkv_tensor* context_lens, float scale, float k_scale, float v_scale, void* workspace,
+                         size_t workspace_bytes, const pkv_tensor* out, void* stream) {
+  if (!k_new) return fail(PKV_ERR_NULL, "k_new: descriptor is NULL");
+  if (!v_new) return fail(PKV_ERR_NULL, "v_new: descriptor is NULL");
+  return pkv::decode_call(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
+                          workspace, workspace_bytes, nullptr, out, stream);
+}
+
+int pkv_suffix_prefill_attn(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_tensor* v_cache,
+                            const pkv_tensor* block_tables, const pkv_tensor* prefix_lens,
+                            const pkv_tensor* suffix_lens, float scale, float k_scale, float v_scale,
+                            const pkv_tensor* out, void* stream) {
+  return prefill_call(q, k_cache, v_cache, block_tables, prefix_lens, suffix_lens, scale, k_scale, v_scale, nullptr,
+                      0, false, out, stream);
+}
+
+size_t pkv_suffix_prefill_workspace_bytes(int64_t total_suffix_tokens, int64_t num_requests, int32_t num_q_heads,
+                                          int32_t num_kv_heads, int32_t head_dim, int64_t max_blocks_per_seq,
+                                          int32_t block_size) {
+  if (total_suffix_tokens < 0 || num_requests < 0 || num_q_heads < 1 || num_kv_heads < 1 ||
+      num_q_heads % num_kv_heads != 0 || head_dim < 1 || max_blocks_per_seq < 1 || block_size < 1)
+    return 0;
+  const int parts = prefill_parts(total_suffix_tokens, num_q_heads, num_kv_heads, max_blocks_per_seq, block_size);
+  return prefill_ws_bytes(parts, total_suffix_tokens, num_q_heads, head_dim);
+}
+
+int pkv_suffix_prefill_attn_split(const pkv_tensor* q, const pkv_tensor* k_cache, const pkv_tensor* v_cache,
+                                  const pkv_tensor* block_tables, const pkv_tensor* prefix_lens,
+                                  const pkv_tensor* suffix_lens, float scale, float k_scale, float v_scale,
+                                  void* workspace, size_t workspace_bytes, const pkv_tensor* out, void* stream) {
+  return prefill_call(q, k_cache, v_cache, block_tables, prefix_lens, suffix_lens, scale, k_scale, v_scale,
+                      workspace, workspace_bytes, true, out, stream);
 }
 
 }  // extern "C"

@@ -83,6 +83,10 @@ struct PrefillParams {
   float* ws_o;                        // [key_splits, S, Hq, D]
   float* ws_ml;                       // [key_splits, S, Hq, 2]
   int32_t key_splits;                 // work-groups sharing one row tile's shared keys
+  // key-split suffix prefill (launch_prefill_split): key_splits parts per row
+  // tile, the first key_splits - 1 on chunks of the prefix's whole stages
+  // (split_prefix_keys), the last on the keys after them; partials go to
+  // ws_o [key_splits, total_rows, Hq, D] and ws_ml [key_splits, total_rows, Hq, 2]
 };
 
 // Cascade decode: the shared keys of a group (L, whole blocks) are cut into
@@ -93,6 +97,11 @@ __host__ __device__ inline int cascade_chunk(int L, int splits) {
   const int c = (L + splits - 1) / splits;
   return (c + kCascadeChunkAlign - 1) / kCascadeChunkAlign * kCascadeChunkAlign;
 }
+
+// Key-split suffix prefill: the prefix keys that the split parts take (whole
+// 64-key stages; the last part takes the rest of the prefix and the suffix),
+// cut into chunks as above.
+__host__ __device__ inline int split_prefix_keys(int P) { return P - P % kCascadeChunkAlign; }
 
 // Supplies a decode workspace of `need` bytes in place of the caller's (the
 // entry point that allocates nothing); returns a pkv_status.
@@ -120,6 +129,10 @@ hipError_t launch_decode_combine(const DecodeParams& p, DT q_dt, DT cache_dt, in
                                  int block_size, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, DT q_dt, DT cache_dt, int head_dim,
                           int block_size, hipStream_t stream);
+// The suffix prefill with its keys split (p.key_splits >= 2 parts per row
+// tile, tiles_per_head counting the parts), then the merge of the parts.
+hipError_t launch_prefill_split(const PrefillParams& p, DT q_dt, DT cache_dt, int head_dim,
+                                int block_size, hipStream_t stream);
 // Cascade decode: the shared part (work-groups [0, shared_wgs), a multiple of
 // 8 and at least sp.hkv * sp.tiles_per_head) and the private-token decode
 // (dp.total_wgs waves, eight per work-group) in one launch, then the combine.

@@ -53,31 +53,142 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   attend_tile<TQ, TC, D, BLK, false>(p, lds, blockIdx.x);
 }
 
+// Key-split form (few rows, long prefixes: a plain launch would leave most
+// CUs idle). Parts 0 .. key_splits-2 of a row tile take chunks of the
+// prefix's whole stages, the last part the keys after them; each writes an
+// unnormalised partial, and prefill_merge_kernel merges them.
 template <typename TQ, typename TC, int D, int BLK>
-hipError_t launch_typed(const PrefillParams& p, hipStream_t stream) {
+__global__ __launch_bounds__(kThreads, 1) void prefill_split_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes<D>];
+  attend_tile<TQ, TC, D, BLK, false, true>(p, lds, blockIdx.x);
+}
+
+// Merge of the key-split parts: one work-group per (suffix token, group of
+// eight query heads), each thread owning 4 consecutive dims of one head. The
+// token's request is found as the prefill finds it (64 requests per round,
+// lengths clamped the same way); the parts that hold keys are the last one
+// and the prefix chunks that reach into the request's prefix, merged by
+// log-sum-exp under a running maximum, eight at a time.
+constexpr int kMergeHeads = 8;
+
+template <typename TQ, int D, int BLK>
+__global__ __launch_bounds__(kMergeHeads * D / 4) void prefill_merge_kernel(PrefillParams p) {
+  const int groups = (p.hq + kMergeHeads - 1) / kMergeHeads;
+  const int64_t t = blockIdx.x / groups;  // packed suffix token
+  const int qh = (blockIdx.x % groups) * kMergeHeads + (int)threadIdx.x / (D / 4);
+  const int d0 = ((int)threadIdx.x % (D / 4)) * 4;
+  const int ln = (int)threadIdx.x % 64;
+  int r = -1;
+  int64_t rows_before = 0;
+  for (int r0 = 0; r0 < p.num_reqs; r0 += 64) {  // uniform over the work-group
+    const int rr = r0 + ln;
+    int64_t s = 0;
+    if (rr < p.num_reqs) s = p.suffix_lens[rr];
+    s = s < 0 ? 0 : (s > p.total_rows ? p.total_rows : s);
+    int64_t incl = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int64_t u = __shfl_up(incl, off);
+      if (ln >= off) incl += u;
+    }
+    const int64_t rb = min(rows_before + (incl - s), p.total_rows);
+    const int64_t re = min(rows_before + incl, p.total_rows);
+    const uint64_t hit = __ballot(rr < p.num_reqs && t >= rb && t < re);
+    if (hit) {
+      r = r0 + __builtin_ctzll(hit);
+      break;
+    }
+    rows_before = min(rows_before + __shfl(incl, 63), p.total_rows);
+  }
+  if (r < 0 || qh >= p.hq) return;  // a row no request covers is left as the plain kernel leaves it
+  const int cap = p.max_blocks * BLK;
+  int P = p.prefix_lens[r];
+  P = P < 0 ? 0 : (P > cap ? cap : P);
+  const int nsplit = p.key_splits - 1;
+  const int Ps = split_prefix_keys(P);
+  const int chunk = cascade_chunk(Ps, nsplit);
+  const int nk = chunk > 0 ? min((Ps + chunk - 1) / chunk, nsplit) : 0;
+  // part list: the last part (it always holds the row's own token), then the
+  // prefix chunks 0 .. nk-1
+  constexpr int kFew = 8;
+  float M = -INFINITY, L = 0.f;
+  f32x4 O = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < nk + 1; j0 += kFew) {
+    f32x2 ml[kFew];
+    f32x4 o[kFew];
+#pragma unroll
+    for (int j = 0; j < kFew; ++j) {
+      const int part = j0 + j == 0 ? nsplit : j0 + j - 1;
+      const int64_t srow = ((int64_t)part * p.total_rows + t) * p.hq + qh;
+      const bool ok = j0 + j < nk + 1;
+      ml[j] = ok ? *reinterpret_cast<const f32x2*>(p.ws_ml + srow * 2) : f32x2{-INFINITY, 0.f};
+      o[j] = ok ? *reinterpret_cast<const f32x4*>(p.ws_o + srow * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float Mb = M;
+#pragma unroll
+    for (int j = 0; j < kFew; ++j) Mb = fmaxf(Mb, ml[j][0]);
+    const float rs = M == Mb ? 1.f : exp2f(M - Mb);
+    L *= rs;
+    O *= rs;
+    M = Mb;
+#pragma unroll
+    for (int j = 0; j < kFew; ++j) {
+      const float f = j0 + j < nk + 1 ? exp2f(ml[j][0] - M) : 0.f;
+      L += ml[j][1] * f;
+      O += o[j] * f;
+    }
+  }
+  const float inv = p.v_scale / L;
+  typedef __attribute__((__vector_size__(4 * sizeof(TQ)))) TQ TQx4;
+  TQx4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = from_f32<TQ>(O[i] * inv);
+  *reinterpret_cast<TQx4*>(reinterpret_cast<TQ*>(p.out) + t * p.o_s0 + (int64_t)qh * p.o_s1 + d0) = v;
+}
+
+template <typename TQ, typename TC, int D, int BLK>
+hipError_t launch_typed(const PrefillParams& p, hipStream_t stream, bool split) {
   const int64_t wgs = (int64_t)p.hkv * p.tiles_per_head;
   if (wgs == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_kernel<TQ, TC, D, BLK>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, p);
+  if (!split) {
+    hipLaunchKernelGGL((prefill_kernel<TQ, TC, D, BLK>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((prefill_split_kernel<TQ, TC, D, BLK>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t mwgs = p.total_rows * ((p.hq + kMergeHeads - 1) / kMergeHeads);
+  hipLaunchKernelGGL((prefill_merge_kernel<TQ, D, BLK>), dim3((unsigned)mwgs), dim3(kMergeHeads * D / 4), 0, stream,
+                     p);
   return hipGetLastError();
 }
 
 template <typename TQ, typename TC>
-hipError_t launch_shape(const PrefillParams& p, int d, int b, hipStream_t s) {
-  if (d == 128 && b == 16) return launch_typed<TQ, TC, 128, 16>(p, s);
-  if (d == 128 && b == 32) return launch_typed<TQ, TC, 128, 32>(p, s);
-  if (d == 64 && b == 16) return launch_typed<TQ, TC, 64, 16>(p, s);
-  if (d == 64 && b == 32) return launch_typed<TQ, TC, 64, 32>(p, s);
+hipError_t launch_shape(const PrefillParams& p, int d, int b, hipStream_t s, bool split) {
+  if (d == 128 && b == 16) return launch_typed<TQ, TC, 128, 16>(p, s, split);
+  if (d == 128 && b == 32) return launch_typed<TQ, TC, 128, 32>(p, s, split);
+  if (d == 64 && b == 16) return launch_typed<TQ, TC, 64, 16>(p, s, split);
+  if (d == 64 && b == 32) return launch_typed<TQ, TC, 64, 32>(p, s, split);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_any(const PrefillParams& p, DT q_dt, DT cache_dt, int d, int b, hipStream_t s, bool split) {
+  if (q_dt == DT::F16 && cache_dt == DT::F16) return launch_shape<f16_t, f16_t>(p, d, b, s, split);
+  if (q_dt == DT::BF16 && cache_dt == DT::BF16) return launch_shape<bf16_t, bf16_t>(p, d, b, s, split);
+  if (q_dt == DT::F16 && cache_dt == DT::FP8) return launch_shape<f16_t, uint8_t>(p, d, b, s, split);
+  if (q_dt == DT::BF16 && cache_dt == DT::FP8) return launch_shape<bf16_t, uint8_t>(p, d, b, s, split);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, DT q_dt, DT cache_dt, int d, int b, hipStream_t s) {
-  if (q_dt == DT::F16 && cache_dt == DT::F16) return launch_shape<f16_t, f16_t>(p, d, b, s);
-  if (q_dt == DT::BF16 && cache_dt == DT::BF16) return launch_shape<bf16_t, bf16_t>(p, d, b, s);
-  if (q_dt == DT::F16 && cache_dt == DT::FP8) return launch_shape<f16_t, uint8_t>(p, d, b, s);
-  if (q_dt == DT::BF16 && cache_dt == DT::FP8) return launch_shape<bf16_t, uint8_t>(p, d, b, s);
-  return hipErrorInvalidValue;
+  return launch_any(p, q_dt, cache_dt, d, b, s, false);
+}
+
+hipError_t launch_prefill_split(const PrefillParams& p, DT q_dt, DT cache_dt, int d, int b, hipStream_t s) {
+  if (p.key_splits < 2 || p.ws_o == nullptr || p.ws_ml == nullptr) return hipErrorInvalidValue;
+  return launch_any(p, q_dt, cache_dt, d, b, s, true);
 }
 
 }  // namespace pkv

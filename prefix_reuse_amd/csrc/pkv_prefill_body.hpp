@@ -253,7 +253,9 @@ constexpr int kLdsBytes = kRing * 2 * kStage * D * 2;
 
 // The rows of one work-group. Returns false (having written nothing) when a
 // kFast pass met a value it cannot convert; the caller then runs the exact pass.
-template <typename TQ, typename TC, int D, int BLK, bool kFast, bool kCasc>
+// kSplit: the suffix prefill with its keys split over several work-groups per
+// row tile (see below); each writes an unnormalised partial for the merge.
+template <typename TQ, typename TC, int D, int BLK, bool kFast, bool kCasc, bool kSplit>
 __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg) {
   typedef Types<TQ, TC, kFast> T;
   typedef typename T::VOp VOp;
@@ -275,7 +277,7 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
   // key_splits work-groups share a row tile, each on one chunk of the keys
   constexpr bool casc = kCasc;  // a kernel of its own: the suffix prefill carries none of it
   int split = 0;
-  if (casc) {
+  if (casc || kSplit) {
     split = tile % p.key_splits;
     tile /= p.key_splits;
   }
@@ -345,6 +347,7 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
   const int S = rows_r / p.group;
   const int cap = p.max_blocks * BLK;
   int P, kv_len, k0 = 0;
+  bool prefix_part = false;  // kSplit: a chunk of the prefix, no mask
   const int32_t* bt;
   if (casc) {  // the group's shared prefix, whole blocks, through its first sequence's table
     P = p.shared_lens[row_base];
@@ -363,6 +366,25 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     kv_len = P + S;
     if (kv_len > cap) kv_len = cap;
     bt = p.block_tables + (int64_t)r * p.bt_s0;
+    if constexpr (kSplit) {
+      // parts 0 .. key_splits-2 take chunks of the prefix's whole stages,
+      // which every suffix row sees in full (no mask); the last part takes
+      // the keys after them, causally, as the unsplit kernel would, with the
+      // table and the prefix length shifted past the chunks
+      const int nsplit = p.key_splits - 1;
+      const int Ps = split_prefix_keys(P);
+      if (split < nsplit) {
+        const int chunk = cascade_chunk(Ps, nsplit);
+        k0 = split * chunk;  // this work-group's keys: k0 .. k0 + kv_len - 1
+        kv_len = max(min(Ps - k0, chunk), 0);
+        if (kv_len > 0) bt += k0 / BLK;
+        prefix_part = true;
+      } else {
+        P -= Ps;
+        kv_len -= Ps;
+        bt += Ps / BLK;
+      }
+    }
   }
 
   const int tid = threadIdx.x;
@@ -383,15 +405,16 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     int c = p.context_lens[row_base + (wq0 + (int)(threadIdx.x % 32)) / p.group] - k0;
     ctx_row = c < 0 ? 0 : (c < kv_len ? c : kv_len);
   }
+  const bool nc = casc || prefix_part;  // every row sees all of this work-group's keys (up to ctx_row)
   int ctx_min_w = ctx_row;
 #pragma unroll
   for (int off = 16; off >= 1; off >>= 1) ctx_min_w = min(ctx_min_w, __shfl_xor(ctx_min_w, off));
-  const int keys_wg = casc ? kv_len : min(kv_len, P + tok_last_wg + 1);
+  const int keys_wg = nc ? kv_len : min(kv_len, P + tok_last_wg + 1);
   const int nst = (keys_wg + kStage - 1) / kStage;
-  const int keys_w = wave_active ? (casc ? kv_len : min(kv_len, P + tok_last_w + 1)) : 0;
+  const int keys_w = wave_active ? (nc ? kv_len : min(kv_len, P + tok_last_w + 1)) : 0;
   const int nsub = (keys_w + 31) / 32;  // 32-key sub-tiles of this wave
   // keys below need no mask in this wave
-  const int full_keys_w = casc ? __builtin_amdgcn_readfirstlane(ctx_min_w) : min(P + tok_first_w + 1, kv_len);
+  const int full_keys_w = nc ? __builtin_amdgcn_readfirstlane(ctx_min_w) : min(P + tok_first_w + 1, kv_len);
   if (nst == 0) return true;  // uniform over the work-group
 
   // ---- Q^T fragments for this lane's row ----
@@ -424,7 +447,7 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
 #pragma unroll
     for (int c = 0; c < QS; ++c) qf[c] = qfrag(c);
   }
-  const int lim = casc ? ctx_row - 1 : P + tok;  // last key position this row may see
+  const int lim = nc ? ctx_row - 1 : P + tok;  // last key position this row may see
   const float c2 = p.qk_scale_log2;
 
   // LDS byte addresses of this lane's operands (buffer 0, sub-tile 0)
@@ -972,7 +995,7 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
     l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
-  if (casc) {  // unnormalised partial (O, m, l) of each (sequence, head) for the combine
+  if (casc || kSplit) {  // unnormalised partial (O, m, l) of each (row, head) for the merge
     if (rvalid) {
       const int64_t srow = ((int64_t)split * p.total_rows + row_base + tok) * p.hq + qh;
       float* orow = p.ws_o + srow * D;
@@ -1007,18 +1030,18 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
 // One row tile. For a bf16 cache the fast pass (V converted to f16 in LDS)
 // reports whether every V value fitted; if one did not, the tile is redone
 // with the exact bf16 hi/lo products.
-template <typename TQ, typename TC, int D, int BLK, bool kCasc>
+template <typename TQ, typename TC, int D, int BLK, bool kCasc, bool kSplit = false>
 __device__ __forceinline__ void attend_tile(const PrefillParams& p, char* lds, int wg) {
   if constexpr (std::is_same<TC, bf16_t>::value) {
-    if (!attend<TQ, TC, D, BLK, true, kCasc>(p, lds, wg)) {
+    if (!attend<TQ, TC, D, BLK, true, kCasc, kSplit>(p, lds, wg)) {
       // rare: redo exactly. The empty asm hides that this pass works on the
       // same work-group, so nothing computed for the fast pass is kept alive
       // for it.
       asm volatile("" : "+s"(wg));
-      attend<TQ, TC, D, BLK, false, kCasc>(p, lds, wg);
+      attend<TQ, TC, D, BLK, false, kCasc, kSplit>(p, lds, wg);
     }
   } else {
-    attend<TQ, TC, D, BLK, false, kCasc>(p, lds, wg);
+    attend<TQ, TC, D, BLK, false, kCasc, kSplit>(p, lds, wg);
   }
 }
 

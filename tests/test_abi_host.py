@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert pkv.abi_version() == 5
+    assert pkv.abi_version() == 6
 
 
 def T(shape, dtype, strides=None, ptr=FAKE):
@@ -167,6 +167,31 @@ def test_prefill_rejects_bad_arguments():
     assert f(R(q), R(kc), R(vc), R(ok_bt), R(pl), R(T([3], I32)), 0.1, 1.0, 1.0, R(q), None) == 3
     assert f(R(q), R(kc), R(vc), R(T([2, 4], I32)), R(pl), R(sl), 0.1, 1.0, 1.0, R(T([9, 4, 64], F16)), None) == 3
     assert f(R(q), R(kc), R(vc), R(ok_bt), R(pl), R(sl), float("nan"), 1.0, 1.0, R(q), None) == 3
+
+
+def test_prefill_split_workspace(monkeypatch):
+    """The key-split prefill's workspace: none for a batch whose row tiles
+    fill the CUs or under PKV_PREFILL_SPLITS=1; parts * total * H_q * (d + 2)
+    floats under a forced count; a call with too small a workspace is
+    refused before anything is launched."""
+    ws = pkv.lib.pkv_suffix_prefill_workspace_bytes
+    assert ws(1600, 16, 32, 8, 128, 125, 16) == 0           # the 16 x (1,900 + 100) batch: 200 work-groups
+    assert ws(10, 1, 32, 7, 128, 100, 16) == 0              # 32 % 7 != 0
+    monkeypatch.setenv("PKV_PREFILL_SPLITS", "1")
+    assert ws(100, 1, 32, 8, 128, 600, 16) == 0
+    monkeypatch.setenv("PKV_PREFILL_SPLITS", "5")
+    assert ws(100, 1, 32, 8, 128, 600, 16) == 5 * 100 * 32 * 130 * 4
+    assert ws(10, 2, 4, 2, 64, 4, 16) == 5 * 10 * 4 * 66 * 4
+    kc, vc = caches()
+    f = pkv.lib.pkv_suffix_prefill_attn_split
+    q, bt, pl, sl = T([10, 4, 64], F16), T([2, 4], I32), T([2], I32), T([2], I32)
+    assert f(R(q), R(kc), R(vc), R(bt), R(pl), R(sl), 0.1, 1.0, 1.0, None, 0, R(q), None) == 6
+    assert "workspace" in err()
+    need = ws(10, 2, 4, 2, 64, 4, 16)
+    assert f(R(q), R(kc), R(vc), R(bt), R(pl), R(sl), 0.1, 1.0, 1.0, FAKE, need - 1, R(q), None) == 6
+    assert f(R(q), R(kc), R(vc), R(bt), R(pl), R(sl), 0.1, 1.0, 1.0, FAKE + 8, need, R(q), None) == 4  # alignment
+    assert f(R(T([10, 4, 64], F32)), R(kc), R(vc), R(bt), R(pl), R(sl), 0.1, 1.0, 1.0, FAKE, need,
+             R(T([10, 4, 64], F32)), None) == 2
 
 
 def test_scale_and_table_limits_are_checked():

@@ -32,7 +32,7 @@ __all__ = [
     "DecodeCase", "PrefillCase", "LongContextFp8Case",
     "make_decode_case", "make_prefill_case",
     "config1_tiny_decode", "config2_llama_decode", "config3_shared_prefix_decode",
-    "config4_suffix_prefill", "config5_long_context_fp8",
+    "config4_suffix_prefill", "next_turn_suffix_prefill", "config5_long_context_fp8",
     "fp8_nan_code",
 ]
 
@@ -332,6 +332,15 @@ def config4_suffix_prefill() -> PrefillCase:
     2,000-block pool in random order."""
     return make_prefill_case(1004, [1900] * 16, [100] * 16, 32, 8, 128, 16, torch.bfloat16,
                              name="suffix-prefill-16x(1900+100)-bf16")
+
+
+def next_turn_suffix_prefill() -> PrefillCase:
+    """One conversation's next turn: one request, 8,000 cached tokens (every
+    earlier turn) + 100 new ones (page "KV Cache에 대해 알아보자" section 5,
+    third limit: each turn of a multi-turn conversation carries all earlier
+    turns, whose K and V are cached), 32/8 heads, d=128, bf16, B=16."""
+    return make_prefill_case(1006, [8000], [100], 32, 8, 128, 16, torch.bfloat16,
+                             name="suffix-prefill-1x(8000+100)-bf16")
 
 
 # ---------------------------------------------------------------------------
