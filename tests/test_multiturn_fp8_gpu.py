@@ -50,8 +50,11 @@ def oracle_pools(emb, pos, tokens):
     return out[0], out[1], np.arange(nblk)[None, :]
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("q_dtype", [torch.bfloat16, torch.float16])
-def test_multiturn_fp8_conversations(q_dtype):
+def test_multiturn_fp8_conversations(q_dtype, split):
+    """split: each turn's suffix prefill through pkv_suffix_prefill_attn_split
+    (one request at a time: the case it is for)."""
     dev = torch.device("cuda")
     emb, pos = tables(91)
     rng = np.random.default_rng(13)
@@ -82,10 +85,10 @@ def test_multiturn_fp8_conversations(q_dtype):
             q = torch.randn(n - p, H_Q, D, generator=g).to(q_dtype)
             bt = torch.zeros(1, 256, dtype=torch.int32)
             bt[0, :len(table)] = torch.tensor(table, dtype=torch.int32)
-            out = pkv.suffix_prefill_attn(q.to(dev), kc, vc, bt.to(dev),
-                                          torch.tensor([p], dtype=torch.int32, device=dev),
-                                          torch.tensor([n - p], dtype=torch.int32, device=dev), scale,
-                                          k_scale=K_SCALE, v_scale=V_SCALE)
+            prefill = pkv.suffix_prefill_attn_split if split else pkv.suffix_prefill_attn
+            out = prefill(q.to(dev), kc, vc, bt.to(dev), torch.tensor([p], dtype=torch.int32, device=dev),
+                          torch.tensor([n - p], dtype=torch.int32, device=dev), scale,
+                          k_scale=K_SCALE, v_scale=V_SCALE)
             torch.cuda.synchronize()
             lk, lv, ident = oracle_pools(emb, pos, conv)
             ref = oracle.suffix_prefill_attention(q.double().numpy(), lk, lv, ident, np.array([p]),
