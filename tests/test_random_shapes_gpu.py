@@ -100,8 +100,9 @@ def test_random_decode_step_and_noalloc(seed):
 
 @pytest.mark.parametrize("seed", range(12))
 def test_random_suffix_prefill(seed):
-    """pkv_suffix_prefill_attn on random requests (up to 6, prefixes 0-1,000,
-    suffixes 0-200), half of them with heavy-tailed key scales."""
+    """pkv_suffix_prefill_attn and pkv_suffix_prefill_attn_split on random
+    requests (up to 6, prefixes 0-1,000, suffixes 0-200), half of them with
+    heavy-tailed key scales."""
     rng = np.random.default_rng(7100 + seed)
     b, d, hq, hkv = _shape(rng)
     kind = _cache_kind(rng)
@@ -120,23 +121,32 @@ def test_random_suffix_prefill(seed):
         kc, vc = nan_fp8_caches(case)
         pkv.append(inp.rows_k.cuda(), inp.rows_v.cuda(), inp.slots.cuda(), kc, vc, inp.k_scale, inp.v_scale)
         q = case.q_suffix.to(q_dtype)
-        out = pkv.suffix_prefill_attn(q.cuda(), kc, vc, case.block_tables.cuda(), case.prefix_lens.cuda(),
-                                      case.suffix_lens.cuda(), case.scale, k_scale=inp.k_scale,
-                                      v_scale=inp.v_scale)
+        args = (q.cuda(), kc, vc, case.block_tables.cuda(), case.prefix_lens.cuda(), case.suffix_lens.cuda(),
+                case.scale)
+        out = pkv.suffix_prefill_attn(*args, k_scale=inp.k_scale, v_scale=inp.v_scale)
+        out_split = pkv.suffix_prefill_attn_split(*args, k_scale=inp.k_scale, v_scale=inp.v_scale)
         torch.cuda.synchronize()
         ek, ev = oracle_fp8_caches(case, inp)
         ref = oracle.suffix_prefill_attention(np64(q), ek, ev, case.block_tables.numpy(), case.prefix_lens.numpy(),
                                               case.suffix_lens.numpy(), case.scale, fp8=True,
                                               k_scale=inp.k_scale, v_scale=inp.v_scale)
         assert report(f"random prefill {seed}", np64(out), ref, q_dtype, TOL["fp8"]) <= 1.0
+        assert report(f"random split prefill {seed}", np64(out_split), ref, q_dtype, TOL["fp8"]) <= 1.0
     else:
         dtype = torch.float16 if kind == "f16" else torch.bfloat16
         case = workloads.make_prefill_case(7100 + seed, plen, slen, hq, hkv, d, b, dtype)
         if heavy:
             _heavy_tailed_keys(case, rng, dtype)
-        out = gpu_prefill(case).out
-        assert np.isfinite(np64(out)).all()
-        assert report(f"random prefill {seed}", np64(out), oracle_prefill(case), dtype, TOL[dtype]) <= 1.0
+        run = gpu_prefill(case)
+        out = run.out
+        out_split = pkv.suffix_prefill_attn_split(case.q_suffix.cuda(), run.k_cache, run.v_cache,
+                                                  case.block_tables.cuda(), case.prefix_lens.cuda(),
+                                                  case.suffix_lens.cuda(), case.scale)
+        torch.cuda.synchronize()
+        assert np.isfinite(np64(out)).all() and np.isfinite(np64(out_split)).all()
+        ref = oracle_prefill(case)
+        assert report(f"random prefill {seed}", np64(out), ref, dtype, TOL[dtype]) <= 1.0
+        assert report(f"random split prefill {seed}", np64(out_split), ref, dtype, TOL[dtype]) <= 1.0
 
 
 @pytest.mark.parametrize("seed", range(8))
