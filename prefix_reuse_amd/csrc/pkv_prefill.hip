@@ -42,6 +42,10 @@
 //    exponentials and moves a row's max only once one of its P values passes
 //    2^6 (an infinite P sends the work-group to the exact pass). The causal mask is applied only
 //    on key tiles that reach past the wave's first token.
+//  * Key-split form (prefill_split_kernel + prefill_merge_kernel), for
+//    batches whose row tiles would leave most CUs idle (one conversation's
+//    next turn): each row tile's keys are spread over several work-groups,
+//    the parts' partials merged by log-sum-exp in a second launch.
 #include "pkv_prefill_body.hpp"
 
 namespace pkv {

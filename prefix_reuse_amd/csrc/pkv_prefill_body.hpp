@@ -273,8 +273,9 @@ __device__ __forceinline__ bool attend(const PrefillParams& p, char* lds, int wg
   const int logical = xcd_remap(wg, p.hkv * p.tiles_per_head);
   const int hk = logical / p.tiles_per_head;
   int tile = logical % p.tiles_per_head;
-  // cascade decode's shared part: the requests are groups of sequences, and
-  // key_splits work-groups share a row tile, each on one chunk of the keys
+  // cascade decode's shared part (the requests are groups of sequences) and
+  // the key-split prefill: key_splits work-groups share a row tile, each on
+  // one part of the keys
   constexpr bool casc = kCasc;  // a kernel of its own: the suffix prefill carries none of it
   int split = 0;
   if (casc || kSplit) {
