@@ -112,19 +112,26 @@ __global__ __launch_bounds__(kMergeHeads * D / 4) void prefill_merge_kernel(Pref
   const int Ps = split_prefix_keys(P);
   const int chunk = cascade_chunk(Ps, nsplit);
   const int nk = chunk > 0 ? min((Ps + chunk - 1) / chunk, nsplit) : 0;
-  // part list: the last part (it always holds the row's own token), then the
-  // prefix chunks 0 .. nk-1
+  // The last part holds keys (at least the first one after the chunks) unless
+  // the prefix filled the table's capacity and that capacity is a whole
+  // number of stages: then every key is in the chunks, the last part's
+  // work-group found nothing to do and its slot was never written.
+  const int skip = (P == cap && Ps == P) ? 1 : 0;
+  const int np = nk + 1 - skip;
+  // part list: the last part (when it holds keys), then the prefix chunks
+  // 0 .. nk-1
   constexpr int kFew = 8;
   float M = -INFINITY, L = 0.f;
   f32x4 O = {0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < nk + 1; j0 += kFew) {
+  for (int j0 = 0; j0 < np; j0 += kFew) {
     f32x2 ml[kFew];
     f32x4 o[kFew];
 #pragma unroll
     for (int j = 0; j < kFew; ++j) {
-      const int part = j0 + j == 0 ? nsplit : j0 + j - 1;
+      const int q = j0 + j + skip;
+      const int part = q == 0 ? nsplit : q - 1;
       const int64_t srow = ((int64_t)part * p.total_rows + t) * p.hq + qh;
-      const bool ok = j0 + j < nk + 1;
+      const bool ok = j0 + j < np;
       ml[j] = ok ? *reinterpret_cast<const f32x2*>(p.ws_ml + srow * 2) : f32x2{-INFINITY, 0.f};
       o[j] = ok ? *reinterpret_cast<const f32x4*>(p.ws_o + srow * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -137,7 +144,7 @@ __global__ __launch_bounds__(kMergeHeads * D / 4) void prefill_merge_kernel(Pref
     M = Mb;
 #pragma unroll
     for (int j = 0; j < kFew; ++j) {
-      const float f = j0 + j < nk + 1 ? exp2f(ml[j][0] - M) : 0.f;
+      const float f = j0 + j < np ? exp2f(ml[j][0] - M) : 0.f;
       L += ml[j][1] * f;
       O += o[j] * f;
     }
