@@ -126,3 +126,25 @@ def test_split_prefill_any_workspace_contents(fill):
     assert report(f"split prefill workspace 0x{fill:02x}", np64(outs[0]), ref, torch.bfloat16,
                   TOL[torch.bfloat16]) <= 1.0
     assert np.array_equal(bits(outs[0]), bits(outs[1]))
+
+
+def test_split_prefill_next_turn_workload_every_row():
+    """The timed next-turn workload (one request, 8,000 cached + 100 new
+    tokens, 32/8 heads, d = 128, bf16, blocks of 16) in the launch
+    configuration the benchmark times: the default part count and a
+    workspace of the queried size, filled with NaN bytes first. Every row
+    against the oracle, and the plain launch's outputs within one rounding."""
+    case = workloads.next_turn_suffix_prefill()
+    need = pkv.suffix_prefill_workspace_bytes(case.q_suffix.shape[0], 1, case.num_q_heads, case.num_kv_heads,
+                                              case.head_dim, case.block_tables.shape[1], case.block_size)
+    print(f"next turn: workspace {need} bytes", flush=True)
+    assert need > 0  # the default takes a split here
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    out = np64(run_split(case, workspace=ws))
+    assert np.isfinite(out).all()
+    assert report("split prefill next turn", out, oracle_prefill(case), torch.bfloat16, TOL[torch.bfloat16]) <= 1.0
+    kc, vc = pkv.caches_from_logical(case.k_pool, case.v_pool, "cuda")
+    pkv.append(case.k_new.cuda(), case.v_new.cuda(), case.slot_mapping.cuda(), kc, vc)
+    plain = np64(pkv.suffix_prefill_attn(case.q_suffix.cuda(), kc, vc, case.block_tables.cuda(),
+                                         case.prefix_lens.cuda(), case.suffix_lens.cuda(), case.scale))
+    assert (np.abs(out - plain) <= 2e-3 + 2 * half_ulp(plain, torch.bfloat16)).all()
