@@ -100,3 +100,48 @@ def test_decode_lengths_past_capacity(max_blocks):
     got = np64(out)
     assert np.isfinite(got).all()
     assert report(f"decode past capacity {cap}", got, ref, torch.float16, TOL[torch.float16]) <= 1.0
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_split_prefill_random_lengths_around_capacity(seed, monkeypatch):
+    """Random capacities (1-39 blocks of 16), 1-4 requests whose prefixes lie
+    within 200 tokens of the capacity (some negative), 0-59 new tokens each,
+    and a forced part count of 2-17: the key-split and plain prefill against
+    the oracle's decode over the cut key counts."""
+    rng = np.random.default_rng(9000 + seed)
+    max_blocks = int(rng.integers(1, 40))
+    cap = max_blocks * B
+    r = int(rng.integers(1, 5))
+    plen = [int(x) for x in rng.integers(max(cap - 200, -10), cap + 200, r)]
+    slen = [int(x) for x in rng.integers(0, 60, r)]
+    if sum(slen) == 0:
+        slen[0] = 1
+    parts = int(rng.integers(2, 18))
+    print(f"seed {seed}: capacity {cap}, P={plen} S={slen}, {parts} parts", flush=True)
+    monkeypatch.setenv("PKV_PREFILL_SPLITS", str(parts))
+    num_blocks = r * max_blocks + 3
+    k_pool, v_pool = pools(seed, num_blocks, torch.bfloat16)
+    bt = table_rows(seed + 1, r, max_blocks, num_blocks)
+    total = sum(slen)
+    g = torch.Generator().manual_seed(seed + 2)
+    q = torch.randn(total, HQ, D, generator=g).to(torch.bfloat16)
+    scale = D ** -0.5
+    kc, vc = pkv.caches_from_logical(k_pool, v_pool, "cuda")
+    args = (q.cuda(), kc, vc, bt.cuda(), torch.tensor(plen, dtype=torch.int32).cuda(),
+            torch.tensor(slen, dtype=torch.int32).cuda(), scale)
+    need = pkv.suffix_prefill_workspace_bytes(total, r, HQ, HKV, D, max_blocks, B)
+    ws = torch.full((max(need, 16),), 0xFF, dtype=torch.uint8, device="cuda")
+    outs = {"split": pkv.suffix_prefill_attn_split(*args, workspace=ws), "plain": pkv.suffix_prefill_attn(*args)}
+    torch.cuda.synchronize()
+    counts, rows_bt = [], []
+    for i_r, (p, s) in enumerate(zip(plen, slen)):
+        pc = min(max(p, 0), cap)
+        for i in range(s):
+            counts.append(min(pc + i + 1, cap))
+            rows_bt.append(bt[i_r])
+    ref = oracle_rows(q, k_pool, v_pool, torch.stack(rows_bt), counts, scale)
+    for name, o in outs.items():
+        got = np64(o)
+        assert np.isfinite(got).all(), name
+        assert report(f"prefill around capacity {seed} ({name})", got, ref, torch.bfloat16,
+                      TOL[torch.bfloat16]) <= 1.0
